@@ -1,0 +1,149 @@
+"""Helpers for the GPU tests: move seeded workloads to the device, call the
+library through its binding, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as wl
+
+TOL = {  # (max-abs, relative Frobenius) gates of the decode output
+    "bf16": (2e-2, 1e-2),
+    "fp8": (5e-2, 3e-2),
+    "fp32": (2e-2, 1e-2),
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def lib():
+    import latent_kv_cache_mla_amd as m
+    return m
+
+
+def to_dev(a: np.ndarray, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def device_inputs(inp: wl.DecodeInputs, max_blocks: int | None = None):
+    """Device tensors for one decode call (paged cache, table, lengths, queries)."""
+    cfg = inp.cfg
+    pool, spool = wl.paged_cache(inp)
+    bt = wl.block_table(inp.seq_lens, inp.page_perm, max_blocks)
+    dev = {
+        "cache": to_dev(pool),
+        "cache_scale": None if spool is None else to_dev(spool.astype(np.float32)),
+        "block_table": to_dev(bt),
+        "seq_lens": to_dev(inp.seq_lens.astype(np.int32)),
+        "n_pages": pool.shape[0],
+        "max_blocks": bt.shape[1],
+    }
+    if cfg.cache_dtype == "fp32":
+        dev["q_abs"] = to_dev(inp.q_abs_f32)
+        dev["q_rope"] = to_dev(inp.q_rope_f32)
+    else:
+        dev["q_abs"] = to_dev(inp.q_abs_bits.view(np.int16)).view(torch.bfloat16)
+        dev["q_rope"] = to_dev(inp.q_rope_bits.view(np.int16)).view(torch.bfloat16)
+    return dev
+
+
+def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: bool = True,
+               plan_separately: bool = False, with_lse: bool = True):
+    """Runs mla_decode on the GPU; returns (o float64 [B,q_len,n_h,d_c], lse)."""
+    m = lib()
+    cfg = inp.cfg
+    dev = dev or device_inputs(inp)
+    q_dt = "fp32" if cfg.cache_dtype == "fp32" else "bf16"
+    desc = m.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
+                         cfg.cache_dtype, q_dt, cfg.out_dtype, num_partitions)
+    ws_bytes = m.mla_decode_workspace_size(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    odt = torch.float32 if cfg.out_dtype == "fp32" else torch.bfloat16
+    o = torch.empty((cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c), dtype=odt, device="cuda")
+    lse = torch.empty((cfg.batch, cfg.q_len, cfg.n_heads), dtype=torch.float32, device="cuda") \
+        if with_lse else None
+    if poison:  # NaN everywhere the call must overwrite, and in its scratch
+        o.fill_(float("nan"))
+        if lse is not None:
+            lse.fill_(float("nan"))
+        ws.fill_(0xFF)
+    if plan_separately:
+        m.mla_decode_plan(desc, dev["seq_lens"], ws)
+        desc.plan_ready = 1
+    m.mla_decode(desc, dev["q_abs"], dev["q_rope"], dev["cache"], dev["cache_scale"],
+                 dev["block_table"], dev["seq_lens"], cfg.softmax_scale, o, lse, ws)
+    torch.cuda.synchronize()
+    o64 = o.float().cpu().numpy().astype(np.float64)
+    lse64 = None if lse is None else lse.cpu().numpy().astype(np.float64)
+    return o64, lse64
+
+
+def oracle_inputs(inp: wl.DecodeInputs, b: int):
+    """fp64 values of what the GPU reads for sequence b (decoded by the oracle)."""
+    cfg = inp.cfg
+    if cfg.cache_dtype == "fp32":
+        lat = inp.lat_f32[b].astype(np.float64)
+        return lat[:, :cfg.d_c], lat[:, cfg.d_c:]
+    if cfg.cache_dtype == "bf16":
+        lat = oracle.bf16_bits_to_f64(inp.lat_bits[b])
+        return lat[:, :cfg.d_c], lat[:, cfg.d_c:]
+    c = oracle.fp8_cache_dequant(inp.lat_codes[b], inp.lat_scales[b])
+    return c, oracle.bf16_bits_to_f64(inp.krope_bits[b])
+
+
+def oracle_queries(inp: wl.DecodeInputs):
+    if inp.cfg.cache_dtype == "fp32":
+        return inp.q_abs_f32.astype(np.float64), inp.q_rope_f32.astype(np.float64)
+    return oracle.bf16_bits_to_f64(inp.q_abs_bits), oracle.bf16_bits_to_f64(inp.q_rope_bits)
+
+
+def oracle_decode(inp: wl.DecodeInputs, batches=None):
+    """Oracle output for all (or some) sequences: (o, lse) float64."""
+    cfg = inp.cfg
+    qa, qr = oracle_queries(inp)
+    idx = range(cfg.batch) if batches is None else batches
+    o = np.zeros((len(idx), cfg.q_len, cfg.n_heads, cfg.d_c))
+    lse = np.zeros((len(idx), cfg.q_len, cfg.n_heads))
+    for k, b in enumerate(idx):
+        c, kr = oracle_inputs(inp, b)
+        r = oracle.latent_attention(qa[b], qr[b], c, kr, cfg.softmax_scale)
+        o[k], lse[k] = r["o"], r["lse"]
+    return o, lse
+
+
+def errors(g: np.ndarray, r: np.ndarray):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    assert np.all(np.isfinite(g)), "non-finite values in the GPU output"
+    max_abs = float(np.max(np.abs(g - r))) if g.size else 0.0
+    nr = float(np.linalg.norm(r))
+    rel_f = float(np.linalg.norm(g - r) / nr) if nr > 0 else float(np.linalg.norm(g - r))
+    return max_abs, rel_f
+
+
+def assert_close(g, r, kind: str, label: str = ""):
+    ma, rf = errors(g, r)
+    tma, trf = TOL[kind]
+    say(f"  [{label}] max-abs {ma:.3e} (gate {tma}), rel-F {rf:.3e} (gate {trf})")
+    assert ma <= tma and rf <= trf, (label, ma, rf)
+    return ma, rf
+
+
+def assert_lse_close(g, r, tol: float, label: str = ""):
+    fin = np.isfinite(r)
+    assert np.array_equal(np.isfinite(g), fin), f"{label}: -inf pattern differs"
+    if fin.any():
+        err = float(np.max(np.abs(g[fin] - r[fin])))
+        say(f"  [{label}] lse max-abs {err:.3e}")
+        assert err <= tol, (label, err)
+    assert np.all(g[~fin] == -np.inf)

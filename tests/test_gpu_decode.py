@@ -1,0 +1,193 @@
+"""Parity of the HIP decode path (through the C ABI) with the CPU oracle.
+
+Every case prints its name and shape before touching the GPU. Gates: bf16
+max-abs 2e-2 / rel-Frobenius 1e-2, fp8 5e-2 / 3e-2, fp32 held to the bf16
+gate plus a tight fp32 check.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+C = wl.CONFIGS
+
+# reduced cases: several 64-token tiles, ragged tails, many splits
+SMALL = {
+    "c2": wl.scaled(C["c2"], batch=3, seq_len=700),
+    "c3": wl.scaled(C["c3"], batch=2, seq_len=5000),
+    "c4": wl.scaled(C["c4"], batch=6, ragged=(1, 2000)),
+    "c5": wl.scaled(C["c5"], batch=4, seq_len=1000),
+}
+
+
+def _kind(cfg):
+    return cfg.cache_dtype
+
+
+def _check(inp, o, lse, label, batches=None):
+    ro, rl = H.oracle_decode(inp, batches)
+    H.assert_close(o, ro, _kind(inp.cfg), label)
+    if lse is not None:
+        H.assert_lse_close(lse, rl, 2e-3, label)
+    return ro
+
+
+def test_tiny_fp32_config():
+    cfg = C["tiny"]
+    H.say(f"case tiny fp32 B={cfg.batch} S={cfg.seq_len} n_h={cfg.n_heads} d_c={cfg.d_c}")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    ro = _check(inp, o, lse, "tiny")
+    ma, rf = H.errors(o, ro)
+    assert rf < 1e-5, rf   # fp32 arithmetic throughout
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_reduced_configs(name):
+    cfg = SMALL[name]
+    H.say(f"case {name}-reduced lens={cfg.seq_len or cfg.ragged} B={cfg.batch} q_len={cfg.q_len}")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    _check(inp, o, lse, f"{name}-reduced")
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size_configs(name):
+    """Full shapes, the launch configuration the benchmark times (automatic
+    partitions). The oracle checks every sequence except for c5, where it
+    checks 16 sampled sequences (both query tokens, all heads and lanes)."""
+    cfg = C[name]
+    H.say(f"case {name}-full B={cfg.batch} q_len={cfg.q_len} ({cfg.cache_dtype})")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    if name == "c5":
+        rng = np.random.default_rng(55)
+        bs = sorted(rng.choice(cfg.batch, 16, replace=False).tolist())
+        _check(inp, o[bs], lse[bs], f"{name}-full-sampled", bs)
+    else:
+        _check(inp, o, lse, f"{name}-full")
+
+
+@pytest.mark.parametrize("parts", [1, 2, 7, 0])
+def test_split_count_invariance(parts):
+    cfg = wl.scaled(C["c2"], batch=2, seq_len=1500)
+    H.say(f"case split-invariance parts={parts}")
+    inp = wl.make_decode_inputs(cfg, q_mult=27.7)
+    o, lse = H.run_decode(inp, num_partitions=parts)
+    _check(inp, o, lse, f"parts={parts}")
+
+
+def test_page_permutation_is_bitwise_invariant():
+    cfg = wl.scaled(C["c2"], batch=3, seq_len=333)
+    H.say("case page-permutation")
+    a = wl.make_decode_inputs(cfg, q_mult=27.7)
+    b = wl.make_decode_inputs(cfg, q_mult=27.7)
+    b.page_perm = np.random.default_rng(9).permutation(len(a.page_perm)).astype(np.int32)
+    oa, la = H.run_decode(a)
+    ob, lb = H.run_decode(b)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_sequence_length_edges(dtype):
+    base = C["c2"] if dtype == "bf16" else wl.scaled(C["c5"], q_len=1)
+    lens = [0, 1, 2, 63, 64, 65, 127, 4097]
+    cfg = wl.scaled(base, batch=len(lens), seq_len=None, ragged=(0, 1))
+    H.say(f"case length-edges {dtype} lens={lens}")
+    inp = wl.make_decode_inputs(cfg, seq_lens=lens, q_mult=27.7)
+    o, lse = H.run_decode(inp)
+    ro = _check(inp, o, lse, f"edges-{dtype}")
+    assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))   # empty sequence
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 65])
+def test_speculative_pair_short_sequences(S):
+    cfg = wl.scaled(C["c5"], batch=2, seq_len=S)
+    H.say(f"case q_len=2 S={S}")
+    inp = wl.make_decode_inputs(cfg, q_mult=27.7)
+    o, lse = H.run_decode(inp)
+    _check(inp, o, lse, f"pair-S{S}")
+    if S == 1:   # the first query of the pair sees nothing
+        assert np.all(o[:, 0] == 0) and np.all(np.isneginf(lse[:, 0]))
+
+
+def test_bitwise_determinism():
+    cfg = wl.scaled(C["c4"], batch=5, ragged=(100, 3000))
+    H.say("case determinism")
+    inp = wl.make_decode_inputs(cfg, q_mult=27.7)
+    dev = H.device_inputs(inp)
+    a = H.run_decode(inp, dev=dev)
+    b = H.run_decode(inp, dev=dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_plan_once_decode_many():
+    cfg = wl.scaled(C["c4"], batch=4, ragged=(10, 900))
+    H.say("case plan-ready")
+    inp = wl.make_decode_inputs(cfg)
+    dev = H.device_inputs(inp)
+    a = H.run_decode(inp, dev=dev)
+    b = H.run_decode(inp, dev=dev, plan_separately=True)
+    assert np.array_equal(a[0], b[0])
+
+
+def test_no_lse_output():
+    cfg = SMALL["c2"]
+    H.say("case lse=NULL")
+    inp = wl.make_decode_inputs(cfg)
+    o, _ = H.run_decode(inp, with_lse=False)
+    _check(inp, o, None, "no-lse")
+
+
+# ----------------------------------------------------------------------------
+# stress self-checks: sharper attention than the gated workloads
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("base", ["c2", "c5"])
+@pytest.mark.parametrize("variant", ["sharp", "rope_only", "content_only", "needle"])
+def test_stress(base, variant):
+    cfg = wl.scaled(SMALL[base], batch=3)
+    H.say(f"case stress {base} {variant}")
+    inp = wl.make_decode_inputs(cfg, q_mult=27.7)
+    if variant == "rope_only":
+        inp.q_abs_bits[...] = 0
+    elif variant == "content_only":
+        inp.q_rope_bits[...] = 0
+    elif variant == "needle":
+        # rope query e_0 for every head, one token per sequence with rope key
+        # 20/scale * e_0: a +20 logit that should take almost all the weight
+        inp.q_rope_bits[...] = 0
+        inp.q_rope_bits[..., 0] = wl.to_bf16_bits(np.array([1.0]))[0]
+        rng = np.random.default_rng(77)
+        for b in range(cfg.batch):
+            j = int(rng.integers(0, inp.seq_lens[b] - cfg.q_len + 1))
+            val = wl.to_bf16_bits(np.array([20.0 / cfg.softmax_scale]))[0]
+            kr = inp.krope_bits[b] if cfg.cache_dtype == "fp8" else inp.lat_bits[b][:, cfg.d_c:]
+            kr[j, :] = 0
+            kr[j, 0] = val
+    o, lse = H.run_decode(inp)
+    _check(inp, o, lse, f"stress-{base}-{variant}")
+
+
+def test_validate_catches_bad_contents():
+    import torch
+    m = H.lib()
+    cfg = wl.scaled(C["c2"], batch=2, seq_len=130)
+    H.say("case validate")
+    inp = wl.make_decode_inputs(cfg)
+    dev = H.device_inputs(inp)
+    desc = m.decode_desc(cfg.batch, 1, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"])
+    m.mla_decode_validate(desc, dev["seq_lens"], dev["block_table"], dev["n_pages"])
+    bad = dev["block_table"].clone()
+    bad[1, 2] = dev["n_pages"]
+    with pytest.raises(m.MlaError) as e:
+        m.mla_decode_validate(desc, dev["seq_lens"], bad, dev["n_pages"])
+    assert e.value.status == m.MLA_ERR_BAD_CONTENTS
+    long = torch.tensor([130, 64 * dev["max_blocks"] + 1], dtype=torch.int32, device="cuda")
+    with pytest.raises(m.MlaError):
+        m.mla_decode_validate(desc, long, dev["block_table"], dev["n_pages"])

@@ -55,10 +55,9 @@ PAGE_SIZE = 64  # tokens per cache page
 
 def to_bf16_bits(x) -> np.ndarray:
     """fp64/fp32 array -> bf16 bit patterns (uint16), via fp32, RNE."""
-    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    import torch
+    f = torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32)))
+    return f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
@@ -67,31 +66,13 @@ def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def _e4m3_positive_table() -> np.ndarray:
-    # finite non-negative e4m3fn values, index == code (0x00..0x7E)
-    vals = np.empty(127, dtype=np.float64)
-    for code in range(127):
-        e, m = code >> 3, code & 7
-        vals[code] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
-    return vals
-
-
-_E4M3_POS = _e4m3_positive_table()
-
-
 def encode_e4m3(x32: np.ndarray) -> np.ndarray:
-    """float32 values -> e4m3fn codes (uint8), RNE, saturating to +-448."""
-    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
-    a = np.minimum(np.abs(x), 448.0)
-    hi = np.searchsorted(_E4M3_POS, a, side="left")
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    dlo = a - _E4M3_POS[lo]
-    dhi = _E4M3_POS[hi] - a
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    code = np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
-    return code
+    """float32 values -> e4m3fn codes (uint8), RNE, saturating to +-448
+    (clamped first, then torch's CPU cast, which rounds to nearest even)."""
+    import torch
+    x = np.clip(np.asarray(x32, dtype=np.float32), -448.0, 448.0)
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
 def quantize_tokens_e4m3(c: np.ndarray):
@@ -275,7 +256,7 @@ def fp8_token_rows(inp: DecodeInputs):
     bf16 bytes (d_c + 2*d_R bytes per token)."""
     out = []
     for codes, kr in zip(inp.lat_codes, inp.krope_bits):
-        out.append(np.concatenate([codes, kr.view(np.uint8).reshape(kr.shape[0], -1)], axis=1))
+        out.append(np.concatenate([codes, kr.view(np.uint8).reshape(kr.shape[0], 2 * kr.shape[1])], axis=1))
     return out
 
 
