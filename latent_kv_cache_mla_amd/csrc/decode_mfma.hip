@@ -1,12 +1,345 @@
-// decode_mfma.hip — placeholder until the matrix-core decode kernel lands.
+// decode_mfma.hip — split-KV absorbed-MLA decode on the gfx950 matrix cores
+// for the DeepSeek attention shape (d_c = 512, d_R = 64, bf16 cache).
+//
+// What it computes (per query row r = (query token m, head i) and cached
+// token j of one sequence):
+//   s_j = scale * (q_abs[r] . c_j + q_rope[r] . k^R_j)      ([LLMsBlog]
+//        "Multi-Head Latent Attention: How Low-Rank KV Compression Scales LLM
+//        Serving", "Query Key Absorption"; [Mishra] "Multi-head Latent
+//        Attention", "Step 4: decoupled RoPE": content and rope dot products
+//        add over the concatenated 576-lane entry)
+//   o[r] = sum_j softmax(s)_j c_j                              ([Zhang]
+//        "Multi-head latent attention", "Value absorption: weight and sum
+//        first, project after": the cached latent is the value)
+// The 128 query rows of a workgroup form the dense dimension of both
+// products, so the cached page is read from HBM once and shared by all rows.
+//
+// Work decomposition:
+//   * workgroup = (page range g, row group of 64 rows); 4 wavefronts, each
+//     owns 16 rows; one workgroup per CU (LDS is sized for it).
+//     Workgroups of one range but different row groups get block ids that
+//     differ by a multiple of 8, so they land on the same XCD and the second
+//     read of a page hits that XCD's L2.
+//   * a 64-token page is one tile. It is copied HBM -> LDS with direct
+//     global-to-LDS loads (no register round trip), double buffered, so the
+//     next page streams in while this one is computed.
+//   * scores: S^T[16 tok x 16 rows] = K[16 x 576] Q^T[576 x 16] with
+//     v_mfma_f32_16x16x32_bf16, tokens as the M dimension: the A operand is
+//     read from LDS (16 bytes per lane), Q^T stays in registers all along.
+//     In this orientation each lane holds 4 tokens of one row per block, so
+//     the row max and sum are mostly in-lane. (16 rows per wavefront keep
+//     O^T + Q^T at 200 registers; gfx950's LDS feeds the 16x16 shape's
+//     doubled operand traffic.)
+//   * online softmax in base 2 with a lazy rescale: the running max only
+//     moves when a tile's max exceeds it by more than 2^8, so the O rescale
+//     is rare; results are exact up to rounding.
+//   * weighted sum: O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16]; P^T comes
+//     straight from the score accumulator registers (converted to bf16), and
+//     V^T is the same LDS page read with the LDS transpose load
+//     (ds_read_b64_tr_b16): keys and values are never materialised.
+//   * the LDS page layout is XOR-swizzled in 16-byte chunks so that both the
+//     row-wise score reads and the transposed value reads are free of bank
+//     conflicts.
 #include "internal.h"
+#include "device_common.h"
 
 namespace mla {
+namespace {
 
-bool mfma_supports(const mla_decode_desc*) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-mla_status launch_decode_mfma(const DecodeArgs&, hipStream_t) {
-  return fail(MLA_ERR_UNSUPPORTED, "mfma decode not built");
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kContentBytes = 64 * 1024;      // 64 tokens x 512 bf16
+constexpr int kRopeBytes = 64 * 128;          // 64 tokens x 64 bf16
+constexpr int kTileBytes = kContentBytes + kRopeBytes;
+constexpr int kRowBytes = 2 * (kDc + kDr);    // one cached token, bf16
+constexpr float kRescaleLog2 = 8.0f;          // lazy-rescale threshold (2^8)
+
+struct MfmaParams {
+  const uint16_t* q_abs;
+  const uint16_t* q_rope;
+  const uint8_t* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* page_start;
+  float* o_part;
+  float* lse_part;
+  float c_log2;  // softmax scale * log2(e)
+  int B, q_len, n_h, max_blocks, rows, row_groups;
+  int64_t G;
+};
+
+// XOR swizzle of the 16-byte chunk index within a content row: a linear map
+// of the token's low 4 bits chosen so that 8 or 16 consecutive tokens at one
+// chunk (score reads), and 4 or 8 consecutive tokens x 2 chunks (transposed
+// value reads), fall in distinct bank groups (32- and 64-bank models).
+__device__ __forceinline__ int swz(int t) { return (t & 15) ^ ((t & 1) ? 12 : 0); }
+// the same for the 8 chunks of a rope row (128-byte rows)
+__device__ __forceinline__ int swz_rope(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// Copy page `page` (tokens [0, n_valid) valid) into LDS buffer `buf`.
+// Wave w copies content rows 16w..16w+15 and rope row groups 2w, 2w+1.
+// Rows past n_valid are read from row 0 so that every LDS value is finite.
+__device__ __forceinline__ void load_tile(const uint8_t* cache, int64_t page, int n_valid,
+                                          uint8_t* buf, int w, int lane) {
+  const uint8_t* pg = cache + page * (64LL * kRowBytes);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = 16 * w + i;
+    const int ts = t < n_valid ? t : 0;
+    const int q = lane ^ swz(t);
+    lds_dma16(pg + ts * kRowBytes + q * 16, buf + t * 1024);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int grp = 2 * w + k;
+    const int t = 8 * grp + (lane >> 3);
+    const int ts = t < n_valid ? t : 0;
+    const int q = (lane & 7) ^ swz_rope(t);
+    lds_dma16(pg + ts * kRowBytes + 2 * kDc + q * 16, buf + kContentBytes + grp * 1024);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
+  // two page buffers as separate objects, used in a statically alternating
+  // order, so that the compiler can tell the prefetch into one from the
+  // reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;   // k-group and column of the 16x16 layouts
+  const int64_t id = blockIdx.x;
+  const int rg = static_cast<int>((id >> 3) % p.row_groups);
+  const int64_t g = (id / (8LL * p.row_groups)) * 8 + (id & 7);
+  if (g >= p.G) return;
+  const int64_t P = p.page_start[p.B];
+  const int64_t pb = range_begin(g, P, p.G), pe = range_begin(g + 1, P, p.G);
+  if (pb >= pe) return;
+
+  int b = 0;
+  {
+    int hi = p.B - 1;
+    while (b < hi) {
+      const int mid = (b + hi) >> 1;
+      if (p.page_start[mid + 1] > pb) hi = mid; else b = mid + 1;
+    }
+  }
+
+  const int my_row = rg * kMfmaRows + w * 16 + l16;     // the row of this lane's columns
+  const int m = my_row / p.n_h, hd = my_row % p.n_h;
+  const float c = p.c_log2;
+
+  // LDS byte offsets of this lane's fragments. The swizzle only changes
+  // offset bits that the unrolled loop constants reach through an XOR, so one
+  // base register per pattern suffices: offset = (base ^ (k << s)) + imm.
+  const int h = swz(l16);
+  // score A-fragment, token 16 tb + l16, content chunk 4 kc + g4:
+  //   bits 6..7 = (kc & 3) ^ (h >> 2), + 256 * (kc >> 2) + 16384 * tb
+  const uint32_t qk_base = l16 * 1024 + ((g4 ^ (h & 3)) << 4) + ((h >> 2) << 6);
+  // rope chunk 4 kk + g4 of a 128-byte rope row: bit 6 = kk ^ (hr >> 2), + 2048 * tb
+  const int hr = swz_rope(l16);
+  const uint32_t rope_base = kContentBytes + l16 * 128 + ((g4 ^ (hr & 3)) << 4) + ((hr >> 2) << 6);
+  // transposed value read, rows 4 g4 + (l16 >> 2) (+16 for the second half of
+  // a 32-token chunk), columns 16 mb + 4 (l16 & 3): bits 5..7 = (mb & 7) ^ (h' >> 1)
+  const int ht = swz(4 * g4 + (l16 >> 2));
+  const uint32_t pv_base = (4 * g4 + (l16 >> 2)) * 1024 + ((((l16 & 3) >> 1) ^ (ht & 1)) << 4) +
+                           (l16 & 1) * 8 + ((ht >> 1) << 5);
+
+  for (; b < p.B && p.page_start[b] < pe; ++b) {
+    const int64_t s0 = p.page_start[b], s1 = p.page_start[b + 1];
+    if (s1 == s0) continue;
+    const int64_t a0 = s0 > pb ? s0 : pb, a1 = s1 < pe ? s1 : pe;
+    const int n_tiles = static_cast<int>(a1 - a0);
+    const int S = clamp_len(p.seq_lens[b], p.max_blocks);
+    const int pidx0 = static_cast<int>(a0 - s0);
+    const int tok1 = min(S, static_cast<int>((a1 - s0) * 64));
+    const int tend = min(tok1, S - p.q_len + m + 1);      // this row's visible end
+    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
+    // page ids of this piece, 64 at a time: lane i holds page (base + i)
+    auto ids_at = [&](int first) {
+      const int k = pidx0 + first + lane;
+      return (first + lane < n_tiles && k < p.max_blocks) ? bt[k] : 0;
+    };
+    int ids_cur = ids_at(0), ids_nxt = ids_at(64);
+
+    // Q^T fragments: per 32-lane k chunk, the lane holds lanes [8 g4, 8 g4 + 8) of its row
+    bf16x8 qf[18];
+    {
+      const int64_t qrow = (static_cast<int64_t>(b) * p.q_len + m) * p.n_h + hd;
+      const bf16x8* qa = reinterpret_cast<const bf16x8*>(p.q_abs + qrow * kDc);
+      const bf16x8* qr = reinterpret_cast<const bf16x8*>(p.q_rope + qrow * kDr);
+#pragma unroll
+      for (int kc = 0; kc < 16; ++kc) qf[kc] = qa[4 * kc + g4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) qf[16 + kk] = qr[4 * kk + g4];
+    }
+
+    f32x4 o[32];
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_lane = 0.f;
+
+    __syncthreads();   // the previous piece's reads of both buffers are done
+    load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), buf0, w, lane);
+
+    // one page: wait for its copy, start the next page's copy into the other
+    // buffer, compute this page
+    auto page = [&](int it, const uint8_t* buf, uint8_t* next) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of page `it`
+      __syncthreads();                      // ... and every other wave's
+      const int pidx = pidx0 + it;
+      if (it + 1 < n_tiles) {
+        if (((it + 1) & 63) == 0) {   // roll the page-id window
+          ids_cur = ids_nxt;
+          ids_nxt = ids_at(it + 65);
+        }
+        load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, (it + 1) & 63),
+                  min(64, tok1 - (pidx + 1) * 64), next, w, lane);
+      }
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        // ---- scores S^T = K Q^T for token blocks 2ch, 2ch+1 (16 each) ----
+        f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+        auto kfrag = [&](int kc, int tb) {
+          const uint32_t off = kc < 16 ? (qk_base ^ ((kc & 3) << 6)) + (kc >> 2) * 256 + tb * 16384
+                                       : (rope_base ^ ((kc - 16) << 6)) + tb * 2048;
+          return *reinterpret_cast<const bf16x8*>(buf + off);
+        };
+        // fragments are read two steps ahead of their MFMAs; the scheduling
+        // barriers pin that order
+        bf16x8 kx[3], ky[3];
+        kx[0] = kfrag(0, 2 * ch);
+        ky[0] = kfrag(0, 2 * ch + 1);
+        kx[1] = kfrag(1, 2 * ch);
+        ky[1] = kfrag(1, 2 * ch + 1);
+#pragma unroll
+        for (int kc = 0; kc < 18; ++kc) {
+          if (kc + 2 < 18) {
+            kx[(kc + 2) % 3] = kfrag(kc + 2, 2 * ch);
+            ky[(kc + 2) % 3] = kfrag(kc + 2, 2 * ch + 1);
+          }
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[kc % 3], qf[kc], sx, 0, 0, 0);
+          sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky[kc % 3], qf[kc], sy, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- scale to log2 units, mask tokens at or past this row's end ----
+        const int tk = pidx * 64 + 32 * ch + 4 * g4;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sx[i] = tk + i < tend ? sx[i] * c : -INFINITY;
+          sy[i] = tk + 16 + i < tend ? sy[i] * c : -INFINITY;
+          mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+        // ---- online softmax (base 2, lazy rescale) ----
+        const float m_new = mx > m_run + kRescaleLog2 ? mx : m_run;
+        const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 0 from -inf
+        m_run = m_new;
+        l_lane *= alpha;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
+        }
+        const float msub = m_run == -INFINITY ? 0.f : m_run;
+        bf16x8 pf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float px = exp2f(sx[i] - msub), py = exp2f(sy[i] - msub);
+          l_lane += px + py;
+          pf[i] = static_cast<__bf16>(px);
+          pf[4 + i] = static_cast<__bf16>(py);
+        }
+
+        // ---- weighted sum O^T += V^T P^T over these 32 tokens ----
+        auto vfrag = [&](int mb) {
+          const uint32_t off = (pv_base ^ ((mb & 7) << 5)) + (mb >> 3) * 256 + ch * 32768;
+          const s16x4 lo = lds_tr16(buf + off);
+          const s16x4 hi = lds_tr16(buf + off + 16384);
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        bf16x8 vf[4];
+        vf[0] = vfrag(0);
+        vf[1] = vfrag(1);
+        vf[2] = vfrag(2);
+#pragma unroll
+        for (int mb = 0; mb < 32; ++mb) {
+          if (mb + 3 < 32) vf[(mb + 3) % 4] = vfrag(mb + 3);
+          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mb % 4], pf, o[mb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+      page(it, buf0, buf1);
+      if (it + 1 < n_tiles) page(it + 1, buf1, buf0);
+    }
+
+    // ---- epilogue: normalised partial and its log-sum-exp ----
+    float l_row = l_lane + __shfl_xor(l_lane, 16, 64);
+    l_row += __shfl_xor(l_row, 32, 64);
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const int64_t slot = slot_of(g, b);
+    float* orow = p.o_part + (slot * p.rows + my_row) * static_cast<int64_t>(kDc);
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) {
+      const f32x4 v = o[mb] * inv;
+      *reinterpret_cast<f32x4*>(orow + mb * 16 + 4 * g4) = v;
+    }
+    if (g4 == 0)
+      p.lse_part[slot * p.rows + my_row] =
+          l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool mfma_supports(const mla_decode_desc* d) {
+  return d->d_c == kDc && d->d_rope == kDr && d->cache_dtype == MLA_BF16 &&
+         d->q_dtype == MLA_BF16 && (static_cast<int64_t>(d->q_len) * d->n_heads) % kMfmaRows == 0;
+}
+
+mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  const mla_decode_desc* d = a.d;
+  MfmaParams p;
+  p.q_abs = static_cast<const uint16_t*>(a.q_abs);
+  p.q_rope = static_cast<const uint16_t*>(a.q_rope);
+  p.cache = static_cast<const uint8_t*>(a.cache);
+  p.block_table = a.block_table;
+  p.seq_lens = a.seq_lens;
+  p.page_start = a.page_start;
+  p.o_part = a.o_part;
+  p.lse_part = a.lse_part;
+  p.c_log2 = a.scale * 1.4426950408889634f;
+  p.B = d->batch;
+  p.q_len = d->q_len;
+  p.n_h = d->n_heads;
+  p.max_blocks = d->max_blocks_per_seq;
+  p.rows = a.p->rows;
+  p.row_groups = a.p->row_groups;
+  p.G = a.p->G;
+  const int64_t g_pad = (a.p->G + 7) / 8 * 8;
+  const dim3 grid(static_cast<unsigned>(g_pad * a.p->row_groups)), block(256);
+  hipLaunchKernelGGL(decode_mfma_bf16, grid, block, 0, st, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
+  return MLA_OK;
 }
 
 }  // namespace mla
