@@ -30,9 +30,13 @@
 //     the row max and sum are mostly in-lane. (16 rows per wavefront keep
 //     O^T + Q^T at 200 registers; gfx950's LDS feeds the 16x16 shape's
 //     doubled operand traffic.)
-//   * online softmax in base 2 with a lazy rescale: the running max only
-//     moves when a tile's max exceeds it by more than 2^8, so the O rescale
-//     is rare; results are exact up to rounding.
+//   * online softmax in base 2 with a lazy reference: probabilities are taken
+//     relative to a running max m that only moves when a tile's max exceeds it
+//     by more than 2^8. Instead of rescaling O then (which would make the
+//     compiler keep the 128 accumulator registers on the VALU side of the
+//     register file), the workgroup restarts the piece from its first page
+//     with the raised m: rare, and exact (O and l are rebuilt against one
+//     reference).
 //   * weighted sum: O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16]; P^T comes
 //     straight from the score accumulator registers (converted to bf16), and
 //     V^T is the same LDS page read with the LDS transpose load
@@ -80,8 +84,14 @@ __device__ __forceinline__ int swz(int t) { return (t & 15) ^ ((t & 1) ? 12 : 0)
 // the same for the 8 chunks of a rope row (128-byte rows)
 __device__ __forceinline__ int swz_rope(int t) { return (t & 7) ^ ((t >> 3) & 1); }
 
-__device__ __forceinline__ void lds_dma16(const void* gsrc, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes from
+// sbase + voff land at LDS address lds + 16 i. Issued as a single instruction
+// so that it is not counted as an LDS access by the compiler's wait-count
+// logic (which would otherwise drain every LDS read while a copy is in
+// flight); its completion is waited for explicitly (vmcnt) before the
+// barrier that publishes the page.
+__device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
@@ -89,38 +99,64 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) s16x4*)(p));
 }
 
-// Copy page `page` (tokens [0, n_valid) valid) into LDS buffer `buf`.
-// Wave w copies content rows 16w..16w+15 and rope row groups 2w, 2w+1.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// Per-lane source offsets of a page copy, precomputed once:
+//   content rows t = 16 j + 4 w + i (j, i in 0..3) need logical chunk
+//   lane ^ swz(t) of the row, and swz depends on t only through 4 w + i, so
+//   four patterns serve all 16 rows of the wave;
+//   rope rows are one per 8 lanes: row 8 (2 w + k) + lane / 8 of the page.
+struct CopyPlan {
+  uint32_t content[4];   // lane byte offset within a content row, per i
+  uint32_t rope[2];      // lane byte offset within the page, per rope group, all rows valid
+};
+
+__device__ __forceinline__ uint32_t rope_src(int w, int k, int lane, int n_valid) {
+  const int t = 8 * (2 * w + k) + (lane >> 3);
+  const int ts = t < n_valid ? t : 0;
+  return ts * kRowBytes + 2 * kDc + (((lane & 7) ^ swz_rope(t)) << 4);
+}
+
+// Copy page `page` (tokens [0, n_valid) valid) into the LDS buffer at `buf`.
 // Rows past n_valid are read from row 0 so that every LDS value is finite.
+// `w` and `n_valid` are wave-uniform: all row arithmetic is scalar.
 __device__ __forceinline__ void load_tile(const uint8_t* cache, int64_t page, int n_valid,
-                                          uint8_t* buf, int w, int lane) {
+                                          uint32_t buf, int w, int lane, const CopyPlan& cp) {
   const uint8_t* pg = cache + page * (64LL * kRowBytes);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = 16 * w + i;
-    const int ts = t < n_valid ? t : 0;
-    const int q = lane ^ swz(t);
-    lds_dma16(pg + ts * kRowBytes + q * 16, buf + t * 1024);
-  }
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int grp = 2 * w + k;
-    const int t = 8 * grp + (lane >> 3);
-    const int ts = t < n_valid ? t : 0;
-    const int q = (lane & 7) ^ swz_rope(t);
-    lds_dma16(pg + ts * kRowBytes + 2 * kDc + q * 16, buf + kContentBytes + grp * 1024);
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * j + 4 * w + i;
+      const int ts = t < n_valid ? t : 0;
+      lds_dma16(pg + ts * kRowBytes, cp.content[i], buf + t * 1024);
+    }
+  if (n_valid == 64) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) lds_dma16(pg, cp.rope[k], buf + kContentBytes + (2 * w + k) * 1024);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      lds_dma16(pg, rope_src(w, k, lane, n_valid), buf + kContentBytes + (2 * w + k) * 1024);
   }
 }
 
 __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
-  // two page buffers as separate objects, used in a statically alternating
-  // order, so that the compiler can tell the prefetch into one from the
-  // reads of the other
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[kTileBytes];
+  // two page buffers: page `it` is computed from buffer it & 1 while page
+  // it + 1 is copied into the other
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
+  __shared__ int restart_flag[2][4];   // per page parity, per wave
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g4 = lane >> 4, l16 = lane & 15;   // k-group and column of the 16x16 layouts
+  CopyPlan cp;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cp.content[i] = (lane ^ swz(4 * w + i)) << 4;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) cp.rope[k] = rope_src(w, k, lane, 64);
   const int64_t id = blockIdx.x;
   const int rg = static_cast<int>((id >> 3) % p.row_groups);
   const int64_t g = (id / (8LL * p.row_groups)) * 8 + (id & 7);
@@ -167,6 +203,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     const int pidx0 = static_cast<int>(a0 - s0);
     const int tok1 = min(S, static_cast<int>((a1 - s0) * 64));
     const int tend = min(tok1, S - p.q_len + m + 1);      // this row's visible end
+    // tokens below tend_all are visible to every row of the wave
+    int tend_all = tend;
+    tend_all = min(tend_all, __shfl_xor(tend_all, 1, 64));
+    tend_all = min(tend_all, __shfl_xor(tend_all, 2, 64));
+    tend_all = min(tend_all, __shfl_xor(tend_all, 4, 64));
+    tend_all = min(tend_all, __shfl_xor(tend_all, 8, 64));
+    tend_all = __builtin_amdgcn_readfirstlane(tend_all);
     const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
     // page ids of this piece, 64 at a time: lane i holds page (base + i)
     auto ids_at = [&](int first) {
@@ -192,14 +235,35 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_lane = 0.f;
 
-    __syncthreads();   // the previous piece's reads of both buffers are done
-    load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), buf0, w, lane);
+    const uint32_t lds0 = lds_addr(smem);
 
-    // one page: wait for its copy, start the next page's copy into the other
-    // buffer, compute this page
-    auto page = [&](int it, const uint8_t* buf, uint8_t* next) {
+    __syncthreads();   // the previous piece's reads of both buffers are done
+    load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0, w,
+              lane, cp);
+
+    for (int it = 0;;) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of page `it`
-      __syncthreads();                      // ... and every other wave's
+      __syncthreads();                      // ... and every other wave's, and their flags
+      if (it > 0) {
+        const int* f = restart_flag[(it - 1) & 1];
+        if (f[0] | f[1] | f[2] | f[3]) {
+          // a row's max rose past the lazy threshold on page it - 1: start
+          // the piece over with the raised maxima (all waves agree)
+#pragma unroll
+          for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          l_lane = 0.f;
+          it = 0;
+          ids_cur = ids_at(0);
+          ids_nxt = ids_at(64);
+          load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0,
+                    w, lane, cp);
+          continue;
+        }
+      }
+      if (it == n_tiles) break;
+      const uint32_t cur = (it & 1) * kTileBytes;
+      const uint8_t* buf = smem + cur;
+      const uint32_t next = lds0 + (kTileBytes - cur);
       const int pidx = pidx0 + it;
       if (it + 1 < n_tiles) {
         if (((it + 1) & 63) == 0) {   // roll the page-id window
@@ -207,8 +271,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
           ids_nxt = ids_at(it + 65);
         }
         load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, (it + 1) & 63),
-                  min(64, tok1 - (pidx + 1) * 64), next, w, lane);
+                  min(64, tok1 - (pidx + 1) * 64), next, w, lane, cp);
       }
+      bool raise = false;   // some row of this wave crossed the lazy threshold
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         // ---- scores S^T = K Q^T for token blocks 2ch, 2ch+1 (16 each) ----
@@ -220,43 +285,53 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
         };
         // fragments are read two steps ahead of their MFMAs; the scheduling
         // barriers pin that order
-        bf16x8 kx[3], ky[3];
-        kx[0] = kfrag(0, 2 * ch);
-        ky[0] = kfrag(0, 2 * ch + 1);
-        kx[1] = kfrag(1, 2 * ch);
-        ky[1] = kfrag(1, 2 * ch + 1);
+        constexpr int kD = 3;   // read distance in steps
+        bf16x8 kx[kD + 1], ky[kD + 1];
+#pragma unroll
+        for (int j = 0; j < kD; ++j) {
+          kx[j] = kfrag(j, 2 * ch);
+          ky[j] = kfrag(j, 2 * ch + 1);
+        }
 #pragma unroll
         for (int kc = 0; kc < 18; ++kc) {
-          if (kc + 2 < 18) {
-            kx[(kc + 2) % 3] = kfrag(kc + 2, 2 * ch);
-            ky[(kc + 2) % 3] = kfrag(kc + 2, 2 * ch + 1);
+          if (kc + kD < 18) {
+            kx[(kc + kD) % (kD + 1)] = kfrag(kc + kD, 2 * ch);
+            ky[(kc + kD) % (kD + 1)] = kfrag(kc + kD, 2 * ch + 1);
           }
-          sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[kc % 3], qf[kc], sx, 0, 0, 0);
-          sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky[kc % 3], qf[kc], sy, 0, 0, 0);
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[kc % (kD + 1)], qf[kc], sx, 0, 0, 0);
+          sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky[kc % (kD + 1)], qf[kc], sy, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
 
         // ---- scale to log2 units, mask tokens at or past this row's end ----
-        const int tk = pidx * 64 + 32 * ch + 4 * g4;
         float mx = -INFINITY;
+        if (pidx * 64 + 32 * ch + 32 <= tend_all) {   // wave-uniform: nothing to mask
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sx[i] = tk + i < tend ? sx[i] * c : -INFINITY;
-          sy[i] = tk + 16 + i < tend ? sy[i] * c : -INFINITY;
-          mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
+          for (int i = 0; i < 4; ++i) {
+            sx[i] *= c;
+            sy[i] *= c;
+            mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
+          }
+        } else {
+          const int tk = pidx * 64 + 32 * ch + 4 * g4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sx[i] = tk + i < tend ? sx[i] * c : -INFINITY;
+            sy[i] = tk + 16 + i < tend ? sy[i] * c : -INFINITY;
+            mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
+          }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
         // ---- online softmax (base 2, lazy rescale) ----
-        const float m_new = mx > m_run + kRescaleLog2 ? mx : m_run;
-        const float alpha = m_new == m_run ? 1.f : exp2f(m_run - m_new);  // 0 from -inf
-        m_run = m_new;
-        l_lane *= alpha;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
+        // rows that already hold weight and see a max above the lazy
+        // threshold force a restart; the others just move their reference
+        if (mx > m_run + kRescaleLog2) {
+          if (m_run != -INFINITY) raise = true;
+          m_run = mx;
         }
+        raise = __any(raise);
         const float msub = m_run == -INFINITY ? 0.f : m_run;
         bf16x8 pf;
 #pragma unroll
@@ -274,21 +349,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
           const s16x4 hi = lds_tr16(buf + off + 16384);
           return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        bf16x8 vf[4];
-        vf[0] = vfrag(0);
-        vf[1] = vfrag(1);
-        vf[2] = vfrag(2);
+        constexpr int kV = 5;   // read distance in steps
+        bf16x8 vf[kV + 1];
+#pragma unroll
+        for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
 #pragma unroll
         for (int mb = 0; mb < 32; ++mb) {
-          if (mb + 3 < 32) vf[(mb + 3) % 4] = vfrag(mb + 3);
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mb % 4], pf, o[mb], 0, 0, 0);
+          if (mb + kV < 32) vf[(mb + kV) % (kV + 1)] = vfrag(mb + kV);
+          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mb % (kV + 1)], pf, o[mb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-    };
-    for (int it = 0; it < n_tiles; it += 2) {
-      page(it, buf0, buf1);
-      if (it + 1 < n_tiles) page(it + 1, buf1, buf0);
+      if (lane == 0) restart_flag[it & 1][w] = raise ? 1 : 0;
+      ++it;
     }
 
     // ---- epilogue: normalised partial and its log-sum-exp ----
