@@ -15,21 +15,24 @@
 // products, so the cached page is read from HBM once and shared by all rows.
 //
 // Work decomposition:
-//   * workgroup = (page range g, row group of 64 rows); 4 wavefronts, each
-//     owns 16 rows; one workgroup per CU (LDS is sized for it).
+//   * workgroup = (page range g, row group of 128 rows); 4 wavefronts, each
+//     owns 32 rows; one workgroup per CU (LDS and registers are sized for
+//     it: O^T fills the 256 accumulation registers, Q^T and the scores live
+//     in the 256 vector registers).
 //     Workgroups of one range but different row groups get block ids that
 //     differ by a multiple of 8, so they land on the same XCD and the second
 //     read of a page hits that XCD's L2.
 //   * a 64-token page is one tile. It is copied HBM -> LDS with direct
 //     global-to-LDS loads (no register round trip), double buffered, so the
 //     next page streams in while this one is computed.
-//   * scores: S^T[16 tok x 16 rows] = K[16 x 576] Q^T[576 x 16] with
-//     v_mfma_f32_16x16x32_bf16, tokens as the M dimension: the A operand is
+//   * scores: S^T[32 tok x 32 rows] = K[32 x 576] Q^T[576 x 32] with
+//     v_mfma_f32_32x32x16_bf16, tokens as the M dimension: the A operand is
 //     read from LDS (16 bytes per lane), Q^T stays in registers all along.
-//     In this orientation each lane holds 4 tokens of one row per block, so
-//     the row max and sum are mostly in-lane. (16 rows per wavefront keep
-//     O^T + Q^T at 200 registers; gfx950's LDS feeds the 16x16 shape's
-//     doubled operand traffic.)
+//     In this orientation each lane holds 16 tokens of one row, so the row
+//     max and sum are in-lane but for one exchange. The score MFMAs are
+//     issued as single asm instructions with vector-register constraints:
+//     that keeps the score accumulator out of the accumulation registers,
+//     which O^T fills.
 //   * online softmax in base 2 with a lazy reference: probabilities are taken
 //     relative to a running max m that only moves when a tile's max exceeds it
 //     by more than 2^8. Instead of rescaling O then (which would make the
@@ -37,7 +40,7 @@
 //     register file), the workgroup restarts the piece from its first page
 //     with the raised m: rare, and exact (O and l are rebuilt against one
 //     reference).
-//   * weighted sum: O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16]; P^T comes
+//   * weighted sum: O^T[512 x 32] += V^T[512 x 32] P^T[32 x 32]; P^T comes
 //     straight from the score accumulator registers (converted to bf16), and
 //     V^T is the same LDS page read with the LDS transpose load
 //     (ds_read_b64_tr_b16): keys and values are never materialised.
@@ -52,6 +55,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDc = 512;
@@ -76,11 +80,29 @@ struct MfmaParams {
   int64_t G;
 };
 
-// XOR swizzle of the 16-byte chunk index within a content row: a linear map
-// of the token's low 4 bits chosen so that 8 or 16 consecutive tokens at one
-// chunk (score reads), and 4 or 8 consecutive tokens x 2 chunks (transposed
-// value reads), fall in distinct bank groups (32- and 64-bank models).
-__device__ __forceinline__ int swz(int t) { return (t & 15) ^ ((t & 1) ? 12 : 0); }
+// XOR swizzle of the 16-byte chunk index within a content row: a map of the
+// token's low 4 bits chosen so that 8 or 16 consecutive tokens at one chunk
+// (score reads), and 4 consecutive tokens x 4 consecutive chunks
+// (transposed value reads), fall in distinct bank groups (32- and 64-bank
+// models).
+__device__ __forceinline__ int swz(int t) {
+  const int v = t & 3, u = (t >> 2) & 3;
+  return ((v >> 1) << 3) | ((v & 1) << 2) | (((v >> 1) ^ (u >> 1)) << 1) | (u & 1);
+}
+
+// Score MFMA S += A B with S in vector registers (see the file comment).
+// The first of a chain starts from zero; the last one of a chain is followed
+// by 16 wait states so that vector ALU reads of S see the final value.
+__device__ __forceinline__ void mfma_s_first(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16& s, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(s) : "v"(a), "v"(b));
+}
 // the same for the 8 chunks of a rope row (128-byte rows)
 __device__ __forceinline__ int swz_rope(int t) { return (t & 7) ^ ((t >> 3) & 1); }
 
@@ -97,6 +119,11 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, u
 __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
+}
+
+__device__ __forceinline__ s16x4 lds_tr16a(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(static_cast<uintptr_t>(a)));
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -151,7 +178,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-  const int g4 = lane >> 4, l16 = lane & 15;   // k-group and column of the 16x16 layouts
+  const int half = lane >> 5, l32 = lane & 31;   // k-group and column of the 32x32 layouts
   CopyPlan cp;
 #pragma unroll
   for (int i = 0; i < 4; ++i) cp.content[i] = (lane ^ swz(4 * w + i)) << 4;
@@ -174,25 +201,33 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     }
   }
 
-  const int my_row = rg * kMfmaRows + w * 16 + l16;     // the row of this lane's columns
+  const int my_row = rg * kMfmaRows + w * 32 + l32;     // the row of this lane's columns
   const int m = my_row / p.n_h, hd = my_row % p.n_h;
   const float c = p.c_log2;
 
   // LDS byte offsets of this lane's fragments. The swizzle only changes
   // offset bits that the unrolled loop constants reach through an XOR, so one
   // base register per pattern suffices: offset = (base ^ (k << s)) + imm.
-  const int h = swz(l16);
-  // score A-fragment, token 16 tb + l16, content chunk 4 kc + g4:
-  //   bits 6..7 = (kc & 3) ^ (h >> 2), + 256 * (kc >> 2) + 16384 * tb
-  const uint32_t qk_base = l16 * 1024 + ((g4 ^ (h & 3)) << 4) + ((h >> 2) << 6);
-  // rope chunk 4 kk + g4 of a 128-byte rope row: bit 6 = kk ^ (hr >> 2), + 2048 * tb
-  const int hr = swz_rope(l16);
-  const uint32_t rope_base = kContentBytes + l16 * 128 + ((g4 ^ (hr & 3)) << 4) + ((hr >> 2) << 6);
-  // transposed value read, rows 4 g4 + (l16 >> 2) (+16 for the second half of
-  // a 32-token chunk), columns 16 mb + 4 (l16 & 3): bits 5..7 = (mb & 7) ^ (h' >> 1)
-  const int ht = swz(4 * g4 + (l16 >> 2));
-  const uint32_t pv_base = (4 * g4 + (l16 >> 2)) * 1024 + ((((l16 & 3) >> 1) ^ (ht & 1)) << 4) +
-                           (l16 & 1) * 8 + ((ht >> 1) << 5);
+  const int hx = swz(l32);
+  // score A-fragment, token 32 ch + l32, content chunk 2 kc + half:
+  //   bits 5..7 = (kc & 7) ^ (hx >> 1), + 256 * (kc >> 3) + 32768 * ch
+  const uint32_t qk_base = l32 * 1024 + ((half ^ (hx & 1)) << 4) + ((hx >> 1) << 5);
+  // rope chunk 2 kk + half of a 128-byte rope row: bits 5..6 = kk ^ (hr >> 1), + 4096 * ch
+  const int hr = swz_rope(l32);
+  const uint32_t rope_base = kContentBytes + l32 * 128 + ((half ^ (hr & 1)) << 4) + ((hr >> 1) << 5);
+  // transposed value reads: 16-lane group G16 = g16, source lane s16 reads
+  // row 4 (g16 >> 1) + (s16 >> 2) (+8 for the second read) of a 16-token
+  // chunk, columns 32 mb + 16 (g16 & 1) + 4 (s16 & 3):
+  //   bits 6..7 = (mb & 3) ^ (swz >> 2), + 256 * (mb >> 2) + 16384 * chunk
+  const int g16 = lane >> 4, s16 = lane & 15;
+  uint32_t pv_base[2];
+#pragma unroll
+  for (int sec = 0; sec < 2; ++sec) {
+    const int t = 4 * (g16 >> 1) + (s16 >> 2) + 8 * sec;
+    const int ht = swz(t);
+    const int qlow = 2 * (g16 & 1) + ((s16 & 3) >> 1);
+    pv_base[sec] = t * 1024 + ((qlow ^ (ht & 3)) << 4) + (s16 & 1) * 8 + ((ht >> 2) << 6);
+  }
 
   for (; b < p.B && p.page_start[b] < pe; ++b) {
     const int64_t s0 = p.page_start[b], s1 = p.page_start[b + 1];
@@ -205,10 +240,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     const int tend = min(tok1, S - p.q_len + m + 1);      // this row's visible end
     // tokens below tend_all are visible to every row of the wave
     int tend_all = tend;
-    tend_all = min(tend_all, __shfl_xor(tend_all, 1, 64));
-    tend_all = min(tend_all, __shfl_xor(tend_all, 2, 64));
-    tend_all = min(tend_all, __shfl_xor(tend_all, 4, 64));
-    tend_all = min(tend_all, __shfl_xor(tend_all, 8, 64));
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) tend_all = min(tend_all, __shfl_xor(tend_all, off, 64));
     tend_all = __builtin_amdgcn_readfirstlane(tend_all);
     const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
     // page ids of this piece, 64 at a time: lane i holds page (base + i)
@@ -216,166 +249,177 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
       const int k = pidx0 + first + lane;
       return (first + lane < n_tiles && k < p.max_blocks) ? bt[k] : 0;
     };
-    int ids_cur = ids_at(0), ids_nxt = ids_at(64);
+    int ids_cur, ids_nxt;
 
-    // Q^T fragments: per 32-lane k chunk, the lane holds lanes [8 g4, 8 g4 + 8) of its row
-    bf16x8 qf[18];
+    // Q^T fragments: per 16-lane k chunk, the lane holds lanes [8 half, 8 half + 8) of its row
+    bf16x8 qf[36];
     {
       const int64_t qrow = (static_cast<int64_t>(b) * p.q_len + m) * p.n_h + hd;
       const bf16x8* qa = reinterpret_cast<const bf16x8*>(p.q_abs + qrow * kDc);
       const bf16x8* qr = reinterpret_cast<const bf16x8*>(p.q_rope + qrow * kDr);
 #pragma unroll
-      for (int kc = 0; kc < 16; ++kc) qf[kc] = qa[4 * kc + g4];
+      for (int kc = 0; kc < 32; ++kc) qf[kc] = qa[2 * kc + half];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) qf[16 + kk] = qr[4 * kk + g4];
+      for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + half];
     }
 
-    f32x4 o[32];
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x16 o[16];
     float m_run = -INFINITY, l_lane = 0.f;
-
     const uint32_t lds0 = lds_addr(smem);
 
-    __syncthreads();   // the previous piece's reads of both buffers are done
-    load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0, w,
-              lane, cp);
-
-    for (int it = 0;;) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of page `it`
-      __syncthreads();                      // ... and every other wave's, and their flags
-      if (it > 0) {
-        const int* f = restart_flag[(it - 1) & 1];
-        if (f[0] | f[1] | f[2] | f[3]) {
-          // a row's max rose past the lazy threshold on page it - 1: start
-          // the piece over with the raised maxima (all waves agree)
+    // The outer loop runs again only when a row's max rose past the lazy
+    // threshold: the piece restarts from its first page with the raised
+    // maxima (every wave sees the same flags, so all restart together).
+    for (bool again = true; again;) {
+      // zero O through the matrix unit: every definition of O is then an
+      // MFMA result, and the compiler keeps O in the accumulation registers
+      // across the page loop (a vector-ALU zero would make it carry O in the
+      // vector registers and copy it in and out on every page)
+      {
+        const bf16x8 z8 = {};
 #pragma unroll
-          for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          l_lane = 0.f;
-          it = 0;
-          ids_cur = ids_at(0);
-          ids_nxt = ids_at(64);
-          load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0,
-                    w, lane, cp);
-          continue;
-        }
+        for (int mb = 0; mb < 16; ++mb)
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z8, z8, f32x16{}, 0, 0, 0);
       }
-      if (it == n_tiles) break;
-      const uint32_t cur = (it & 1) * kTileBytes;
-      const uint8_t* buf = smem + cur;
-      const uint32_t next = lds0 + (kTileBytes - cur);
-      const int pidx = pidx0 + it;
-      if (it + 1 < n_tiles) {
-        if (((it + 1) & 63) == 0) {   // roll the page-id window
-          ids_cur = ids_nxt;
-          ids_nxt = ids_at(it + 65);
-        }
-        load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, (it + 1) & 63),
-                  min(64, tok1 - (pidx + 1) * 64), next, w, lane, cp);
-      }
-      bool raise = false;   // some row of this wave crossed the lazy threshold
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        // ---- scores S^T = K Q^T for token blocks 2ch, 2ch+1 (16 each) ----
-        f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
-        auto kfrag = [&](int kc, int tb) {
-          const uint32_t off = kc < 16 ? (qk_base ^ ((kc & 3) << 6)) + (kc >> 2) * 256 + tb * 16384
-                                       : (rope_base ^ ((kc - 16) << 6)) + tb * 2048;
-          return *reinterpret_cast<const bf16x8*>(buf + off);
-        };
-        // fragments are read two steps ahead of their MFMAs; the scheduling
-        // barriers pin that order
-        constexpr int kD = 3;   // read distance in steps
-        bf16x8 kx[kD + 1], ky[kD + 1];
-#pragma unroll
-        for (int j = 0; j < kD; ++j) {
-          kx[j] = kfrag(j, 2 * ch);
-          ky[j] = kfrag(j, 2 * ch + 1);
-        }
-#pragma unroll
-        for (int kc = 0; kc < 18; ++kc) {
-          if (kc + kD < 18) {
-            kx[(kc + kD) % (kD + 1)] = kfrag(kc + kD, 2 * ch);
-            ky[(kc + kD) % (kD + 1)] = kfrag(kc + kD, 2 * ch + 1);
-          }
-          sx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kx[kc % (kD + 1)], qf[kc], sx, 0, 0, 0);
-          sy = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ky[kc % (kD + 1)], qf[kc], sy, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      l_lane = 0.f;
+      again = false;
+      ids_cur = ids_at(0);
+      ids_nxt = ids_at(64);
+      __syncthreads();   // earlier reads of both buffers are done
+      load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0, w,
+                lane, cp);
 
-        // ---- scale to log2 units, mask tokens at or past this row's end ----
-        float mx = -INFINITY;
-        if (pidx * 64 + 32 * ch + 32 <= tend_all) {   // wave-uniform: nothing to mask
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sx[i] *= c;
-            sy[i] *= c;
-            mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
-          }
-        } else {
-          const int tk = pidx * 64 + 32 * ch + 4 * g4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sx[i] = tk + i < tend ? sx[i] * c : -INFINITY;
-            sy[i] = tk + 16 + i < tend ? sy[i] * c : -INFINITY;
-            mx = fmaxf(mx, fmaxf(sx[i], sy[i]));
+      for (int it = 0;; ++it) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of page `it`
+        __syncthreads();                      // ... and every other wave's, and their flags
+        if (it > 0) {
+          const int* f = restart_flag[(it - 1) & 1];
+          if (f[0] | f[1] | f[2] | f[3]) {
+            again = true;
+            break;
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (it == n_tiles) break;
+        const uint32_t cur = (it & 1) * kTileBytes;
+        const uint32_t next = lds0 + (kTileBytes - cur);
+        // this page's fragment bases (cur only sets bits 13 and 16, which the
+        // XOR constants below never touch)
+        const uint32_t qk_pg = lds0 + cur + qk_base, rope_pg = lds0 + cur + rope_base;
+        const uint32_t pv_pg0 = lds0 + cur + pv_base[0], pv_pg1 = lds0 + cur + pv_base[1];
+        const int pidx = pidx0 + it;
+        if (it + 1 < n_tiles) {
+          if (((it + 1) & 63) == 0) {   // roll the page-id window
+            ids_cur = ids_nxt;
+            ids_nxt = ids_at(it + 65);
+          }
+          load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, (it + 1) & 63),
+                    min(64, tok1 - (pidx + 1) * 64), next, w, lane, cp);
+        }
+        bool raise = false;   // some row of this wave crossed the lazy threshold
 
-        // ---- online softmax (base 2, lazy rescale) ----
-        // rows that already hold weight and see a max above the lazy
-        // threshold force a restart; the others just move their reference
-        if (mx > m_run + kRescaleLog2) {
-          if (m_run != -INFINITY) raise = true;
-          m_run = mx;
-        }
-        raise = __any(raise);
-        const float msub = m_run == -INFINITY ? 0.f : m_run;
-        bf16x8 pf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float px = exp2f(sx[i] - msub), py = exp2f(sy[i] - msub);
-          l_lane += px + py;
-          pf[i] = static_cast<__bf16>(px);
-          pf[4 + i] = static_cast<__bf16>(py);
-        }
+        for (int ch = 0; ch < 2; ++ch) {
+          // ---- scores S^T = K Q^T for tokens [32 ch, 32 ch + 32) ----
+          // the per-half bases differ in the expression, so nothing is shared
+          // (and kept live) across the halves
+          const uint32_t qk_h = ch ? (qk_pg + 32768) : qk_pg;
+          const uint32_t rope_h = ch ? (rope_pg + 4096) : rope_pg;
+          auto kfrag = [&](int kc) {
+            const uint32_t a = kc < 32 ? (qk_h ^ ((kc & 7) << 5)) + (kc >> 3) * 256
+                                       : rope_h ^ ((kc - 32) << 5);
+            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                static_cast<uintptr_t>(a));
+          };
+          // A fragments are read kD steps ahead of their MFMAs; the
+          // scheduling barriers pin that order
+          constexpr int kD = 3;
+          bf16x8 kf[kD + 1];
+#pragma unroll
+          for (int j = 0; j < kD; ++j) kf[j] = kfrag(j);
+          f32x16 sc;
+#pragma unroll
+          for (int kc = 0; kc < 36; ++kc) {
+            if (kc + kD < 36) kf[(kc + kD) % (kD + 1)] = kfrag(kc + kD);
+            if (kc == 0) mfma_s_first(sc, kf[0], qf[0]);
+            else if (kc == 35) mfma_s_last(sc, kf[kc % (kD + 1)], qf[kc]);
+            else mfma_s(sc, kf[kc % (kD + 1)], qf[kc]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
 
-        // ---- weighted sum O^T += V^T P^T over these 32 tokens ----
-        auto vfrag = [&](int mb) {
-          const uint32_t off = (pv_base ^ ((mb & 7) << 5)) + (mb >> 3) * 256 + ch * 32768;
-          const s16x4 lo = lds_tr16(buf + off);
-          const s16x4 hi = lds_tr16(buf + off + 16384);
-          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        };
-        constexpr int kV = 5;   // read distance in steps
-        bf16x8 vf[kV + 1];
+          // ---- scale to log2 units, mask tokens at or past this row's end ----
+          float mx = -INFINITY;
+          if (pidx * 64 + 32 * ch + 32 <= tend_all) {   // wave-uniform: nothing to mask
 #pragma unroll
-        for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
+            for (int r = 0; r < 16; ++r) {
+              sc[r] *= c;
+              mx = fmaxf(mx, sc[r]);
+            }
+          } else {
+            const int tk = pidx * 64 + 32 * ch + 4 * half;
 #pragma unroll
-        for (int mb = 0; mb < 32; ++mb) {
-          if (mb + kV < 32) vf[(mb + kV) % (kV + 1)] = vfrag(mb + kV);
-          o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[mb % (kV + 1)], pf, o[mb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 16; ++r) {
+              sc[r] = tk + (r & 3) + 8 * (r >> 2) < tend ? sc[r] * c : -INFINITY;
+              mx = fmaxf(mx, sc[r]);
+            }
+          }
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+
+          // ---- online softmax (base 2, lazy reference) ----
+          // rows that already hold weight and see a max above the lazy
+          // threshold force a restart; the others just move their reference
+          if (mx > m_run + kRescaleLog2) {
+            if (m_run != -INFINITY) raise = true;
+            m_run = mx;
+          }
+          raise = __any(raise);
+          const float msub = m_run == -INFINITY ? 0.f : m_run;
+          bf16x8 pf[2];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(sc[r] - msub);
+            l_lane += pr;
+            pf[r >> 3][r & 7] = static_cast<__bf16>(pr);
+          }
+
+          // ---- weighted sum O^T += V^T P^T over these 32 tokens ----
+          const uint32_t pv_h0 = ch ? (pv_pg0 + 32768) : pv_pg0;
+          const uint32_t pv_h1 = ch ? (pv_pg1 + 32768) : pv_pg1;
+          auto vfrag = [&](int st) {
+            const int mb = st >> 1, cc = st & 1;
+            const uint32_t off = (mb >> 2) * 256 + cc * 16384;
+            const s16x4 lo = lds_tr16a((pv_h0 ^ ((mb & 3) << 6)) + off);
+            const s16x4 hi = lds_tr16a((pv_h1 ^ ((mb & 3) << 6)) + off);
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          };
+          constexpr int kV = 3;   // read distance in steps
+          bf16x8 vf[kV + 1];
+#pragma unroll
+          for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
+#pragma unroll
+          for (int st = 0; st < 32; ++st) {
+            if (st + kV < 32) vf[(st + kV) % (kV + 1)] = vfrag(st + kV);
+            o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % (kV + 1)], pf[st & 1],
+                                                                   o[st >> 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+        if (lane == 0) restart_flag[it & 1][w] = raise ? 1 : 0;
       }
-      if (lane == 0) restart_flag[it & 1][w] = raise ? 1 : 0;
-      ++it;
     }
 
     // ---- epilogue: normalised partial and its log-sum-exp ----
-    float l_row = l_lane + __shfl_xor(l_lane, 16, 64);
-    l_row += __shfl_xor(l_row, 32, 64);
+    const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const int64_t slot = slot_of(g, b);
     float* orow = p.o_part + (slot * p.rows + my_row) * static_cast<int64_t>(kDc);
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      const f32x4 v = o[mb] * inv;
-      *reinterpret_cast<f32x4*>(orow + mb * 16 + 4 * g4) = v;
-    }
-    if (g4 == 0)
+    for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = f32x4{o[mb][4 * j], o[mb][4 * j + 1], o[mb][4 * j + 2], o[mb][4 * j + 3]} * inv;
+        *reinterpret_cast<f32x4*>(orow + mb * 32 + 4 * half + 8 * j) = v;
+      }
+    if (half == 0)
       p.lse_part[slot * p.rows + my_row] =
           l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
   }

@@ -13,7 +13,7 @@ namespace mla {
 // query) so that workspace sizes are a pure function of the descriptor.
 constexpr int kNumCUs = 256;
 // Rows (query token x head) one workgroup of the MFMA decode kernel covers.
-constexpr int kMfmaRows = 64;
+constexpr int kMfmaRows = 128;
 // Rows one workgroup of the generic decode kernel covers (one per wavefront).
 constexpr int kGenericRows = 4;
 
