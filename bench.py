@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for 600 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB three times (untimed), "
+                         "so that hardware byte counters can be scaled against a known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -199,6 +202,14 @@ def main():
                      "traffic": traffic, "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes_per_launch": cache_bytes},
     }
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
