@@ -70,6 +70,7 @@ mla_status make_plan(const mla_decode_desc* d, DecodePlan* p) {
     return fail(MLA_ERR_UNSUPPORTED, "grid too large");
   p->G = G;
   p->slots = G + d->batch;
+  p->part_bf16 = (p->path == Path::Mfma && d->out_dtype == MLA_BF16) ? 1 : 0;
   p->plan_off = 0;
   p->opart_off = align256(sizeof(int32_t) * (static_cast<size_t>(d->batch) + 1));
   p->lse_off = align256(p->opart_off + sizeof(float) * static_cast<size_t>(p->slots) * rows * d->d_c);
@@ -142,7 +143,7 @@ mla_status prepare(const mla_decode_desc* d, const void* q_abs, const void* q_ro
   a->seq_lens = seq_lens;
   a->page_start = reinterpret_cast<const int32_t*>(ws + p->plan_off);
   a->scale = scale;
-  a->o_part = reinterpret_cast<float*>(ws + p->opart_off);
+  a->o_part = ws + p->opart_off;
   a->lse_part = reinterpret_cast<float*>(ws + p->lse_off);
   a->o_latent = nullptr;
   a->lse_out = nullptr;
@@ -211,7 +212,7 @@ mla_status mla_decode_combine(const mla_decode_desc* d, void* workspace, size_t 
   a.d = d;
   a.p = &p;
   a.page_start = reinterpret_cast<const int32_t*>(ws + p.plan_off);
-  a.o_part = reinterpret_cast<float*>(ws + p.opart_off);
+  a.o_part = ws + p.opart_off;
   a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
   a.o_latent = o_latent;
   a.lse_out = lse_out;

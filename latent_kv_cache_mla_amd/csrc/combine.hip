@@ -40,63 +40,92 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (t == 1023) page_start[B] = part[1023];
 }
 
-template <int OT>  // output dtype
-__global__ __launch_bounds__(128) void combine_kernel(const int32_t* __restrict__ page_start,
-                                                      const float* __restrict__ o_part,
+// 8 consecutive partial elements of one row, as fp32
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 x = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+
+// One wavefront per output row (sequence b, row r): the lanes first reduce
+// the row's per-range log-sum-exps, then each lane combines 8 consecutive
+// latent lanes over the ranges.
+template <typename PT, int OT>  // partial element type, output dtype
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
+                                                      const PT* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       void* __restrict__ o_latent,
                                                       float* __restrict__ lse_out,
                                                       int B, int rows, int d_c, int64_t G) {
-  const int64_t b = blockIdx.x / rows;
-  const int r = static_cast<int>(blockIdx.x % rows);
+  const int lane = threadIdx.x & 63;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (pair >= static_cast<int64_t>(B) * rows) return;
+  const int64_t b = pair / rows;
+  const int r = static_cast<int>(pair % rows);
   const int64_t P = page_start[B];
   const int64_t s0 = page_start[b], s1 = page_start[b + 1];
-  const int64_t out_row = (b * rows + r) * static_cast<int64_t>(d_c);
+  const int64_t out_row = pair * d_c;
 
-  int64_t glo = 0, ghi = -1;
-  float mx = -INFINITY;
+  // ranges [glo, ghi] hold the sequence's pages; with more ranges than pages
+  // some ranges are empty and wrote nothing
+  int64_t glo = 0, n = 0;
   if (s1 > s0) {
     glo = range_of_page(s0, P, G);
-    ghi = range_of_page(s1 - 1, P, G);
-    for (int64_t g = glo; g <= ghi; ++g) {
-      if (range_begin(g + 1, P, G) == range_begin(g, P, G)) continue;  // empty range
-      mx = fmaxf(mx, lse_part[slot_of(g, b) * rows + r]);
-    }
+    n = range_of_page(s1 - 1, P, G) - glo + 1;
   }
+  const bool may_be_empty = G > P;
+  auto lse_of = [&](int64_t j) {
+    const int64_t g = glo + j;
+    if (may_be_empty && range_begin(g + 1, P, G) == range_begin(g, P, G)) return -INFINITY;
+    return lse_part[slot_of(g, b) * rows + r];
+  };
+  float mx = -INFINITY;
+  for (int64_t j = lane; j < n; j += 64) mx = fmaxf(mx, lse_of(j));
+  mx = wave_max(mx);
   float wsum = 0.f;
   if (mx != -INFINITY)
-    for (int64_t g = glo; g <= ghi; ++g) {
-      if (range_begin(g + 1, P, G) == range_begin(g, P, G)) continue;
-      const float l = lse_part[slot_of(g, b) * rows + r];
+    for (int64_t j = lane; j < n; j += 64) {
+      const float l = lse_of(j);
       if (l != -INFINITY) wsum += expf(l - mx);
     }
+  wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  for (int k0 = threadIdx.x * 4; k0 < d_c; k0 += 512) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  for (int c0 = 8 * lane; c0 < d_c; c0 += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (mx != -INFINITY) {
-      for (int64_t g = glo; g <= ghi; ++g) {
-        if (range_begin(g + 1, P, G) == range_begin(g, P, G)) continue;
-        const int64_t slot = slot_of(g, b);
-        const float l = lse_part[slot * rows + r];
+      for (int64_t j = 0; j < n; ++j) {
+        const float l = lse_of(j);   // wave-uniform
         if (l == -INFINITY) continue;
         const float wgt = expf(l - mx) * inv;
-        const float4 v = *reinterpret_cast<const float4*>(o_part + (slot * rows + r) * static_cast<int64_t>(d_c) + k0);
-        acc.x = fmaf(wgt, v.x, acc.x);
-        acc.y = fmaf(wgt, v.y, acc.y);
-        acc.z = fmaf(wgt, v.z, acc.z);
-        acc.w = fmaf(wgt, v.w, acc.w);
+        float v[8];
+        load8(o_part + (slot_of(glo + j, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
       }
     }
     if constexpr (OT == MLA_FP32) {
-      *reinterpret_cast<float4*>(static_cast<float*>(o_latent) + out_row + k0) = acc;
+      float* o = static_cast<float*>(o_latent) + out_row + c0;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     } else {
-      const uint32_t lo = f32_to_bf16(acc.x) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
-      const uint32_t hi = f32_to_bf16(acc.z) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(o_latent) + out_row + k0) = make_uint2(lo, hi);
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        u[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(o_latent) + out_row + c0) =
+          make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
-  if (lse_out != nullptr && threadIdx.x == 0)
-    lse_out[b * rows + r] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  if (lse_out != nullptr && lane == 0) lse_out[pair] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 }  // namespace
@@ -111,13 +140,26 @@ mla_status launch_plan(const int32_t* seq_lens, int B, int max_blocks, int32_t* 
 
 mla_status launch_combine(const DecodeArgs& a, hipStream_t st) {
   const int B = a.d->batch, rows = a.p->rows;
-  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(B) * rows)), block(128);
-  if (a.d->out_dtype == MLA_FP32)
-    hipLaunchKernelGGL(combine_kernel<MLA_FP32>, grid, block, 0, st, a.page_start, a.o_part,
-                       a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
-  else
-    hipLaunchKernelGGL(combine_kernel<MLA_BF16>, grid, block, 0, st, a.page_start, a.o_part,
-                       a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+  const int64_t pairs = static_cast<int64_t>(B) * rows;
+  const dim3 grid(static_cast<unsigned>((pairs + 3) / 4)), block(256);
+  const bool bf16_out = a.d->out_dtype == MLA_BF16;
+  if (a.p->part_bf16) {
+    const uint16_t* op = static_cast<const uint16_t*>(a.o_part);
+    if (bf16_out)
+      hipLaunchKernelGGL((combine_kernel<uint16_t, MLA_BF16>), grid, block, 0, st, a.page_start, op,
+                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+    else
+      hipLaunchKernelGGL((combine_kernel<uint16_t, MLA_FP32>), grid, block, 0, st, a.page_start, op,
+                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+  } else {
+    const float* op = static_cast<const float*>(a.o_part);
+    if (bf16_out)
+      hipLaunchKernelGGL((combine_kernel<float, MLA_BF16>), grid, block, 0, st, a.page_start, op,
+                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, MLA_FP32>), grid, block, 0, st, a.page_start, op,
+                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
   return MLA_OK;

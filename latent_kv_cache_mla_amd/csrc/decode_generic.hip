@@ -185,7 +185,7 @@ mla_status launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
   p.block_table = a.block_table;
   p.seq_lens = a.seq_lens;
   p.page_start = a.page_start;
-  p.o_part = a.o_part;
+  p.o_part = static_cast<float*>(a.o_part);
   p.lse_part = a.lse_part;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.B = d->batch;

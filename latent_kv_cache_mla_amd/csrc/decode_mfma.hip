@@ -19,34 +19,44 @@
 //     owns 32 rows; one workgroup per CU (LDS and registers are sized for
 //     it: O^T fills the 256 accumulation registers, Q^T and the scores live
 //     in the 256 vector registers).
-//     Workgroups of one range but different row groups get block ids that
-//     differ by a multiple of 8, so they land on the same XCD and the second
-//     read of a page hits that XCD's L2.
-//   * a 64-token page is one tile. It is copied HBM -> LDS with direct
-//     global-to-LDS loads (no register round trip), double buffered, so the
-//     next page streams in while this one is computed.
+//   * block ids are mapped so that each XCD (ids congruent mod 8) receives a
+//     contiguous run of ranges: the ranges of one sequence, and the row
+//     groups of one range, then share that XCD's L2 for the queries and the
+//     pages.
+//   * the cache streams through LDS in 32-token chunks (half a page) held in
+//     a ring of four stages. Chunks are copied HBM -> LDS with direct
+//     global-to-LDS loads (no register round trip); two chunks are always in
+//     flight while one is being multiplied against the queries and the one
+//     before it against the probabilities.
 //   * scores: S^T[32 tok x 32 rows] = K[32 x 576] Q^T[576 x 32] with
 //     v_mfma_f32_32x32x16_bf16, tokens as the M dimension: the A operand is
 //     read from LDS (16 bytes per lane), Q^T stays in registers all along.
 //     In this orientation each lane holds 16 tokens of one row, so the row
-//     max and sum are in-lane but for one exchange. The score MFMAs are
-//     issued as single asm instructions with vector-register constraints:
-//     that keeps the score accumulator out of the accumulation registers,
-//     which O^T fills.
+//     max and sum are in-lane but for one exchange between the wave halves.
+//     The score MFMAs are issued as single asm instructions with
+//     vector-register constraints: that keeps the score accumulator out of
+//     the accumulation registers, which O^T fills.
+//   * software pipeline per chunk k: the score MFMAs of chunk k are
+//     interleaved with the vector-ALU softmax of chunk k - 1 (scale, mask,
+//     row max, exponentials, bf16 packing), then the weighted sum of chunk
+//     k - 1 runs on the matrix unit. The matrix unit is thus never idle
+//     while the softmax is computed.
 //   * online softmax in base 2 with a lazy reference: probabilities are taken
-//     relative to a running max m that only moves when a tile's max exceeds it
-//     by more than 2^8. Instead of rescaling O then (which would make the
+//     relative to a running max m that only moves when a chunk's max exceeds
+//     it by more than 2^8. Instead of rescaling O then (which would make the
 //     compiler keep the 128 accumulator registers on the VALU side of the
-//     register file), the workgroup restarts the piece from its first page
+//     register file), the workgroup restarts the piece from its first chunk
 //     with the raised m: rare, and exact (O and l are rebuilt against one
 //     reference).
 //   * weighted sum: O^T[512 x 32] += V^T[512 x 32] P^T[32 x 32]; P^T comes
-//     straight from the score accumulator registers (converted to bf16), and
-//     V^T is the same LDS page read with the LDS transpose load
-//     (ds_read_b64_tr_b16): keys and values are never materialised.
-//   * the LDS page layout is XOR-swizzled in 16-byte chunks so that both the
+//     straight from the score registers (converted to bf16), and V^T is the
+//     same LDS chunk read with the LDS transpose load (ds_read_b64_tr_b16):
+//     keys and values are never materialised.
+//   * the LDS chunk layout is XOR-swizzled in 16-byte units so that both the
 //     row-wise score reads and the transposed value reads are free of bank
 //     conflicts.
+#include <type_traits>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -57,25 +67,21 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDc = 512;
 constexpr int kDr = 64;
-constexpr int kContentBytes = 64 * 1024;      // 64 tokens x 512 bf16
-constexpr int kRopeBytes = 64 * 128;          // 64 tokens x 64 bf16
-constexpr int kTileBytes = kContentBytes + kRopeBytes;
-constexpr int kRowBytes = 2 * (kDc + kDr);    // one cached token, bf16
-constexpr float kRescaleLog2 = 8.0f;          // lazy-rescale threshold (2^8)
+constexpr int kChunk = 32;                           // tokens per pipeline stage
+constexpr int kChunkContent = kChunk * 2 * kDc;      // 32 tokens x 512 bf16
+constexpr int kChunkBytes = kChunkContent + kChunk * 2 * kDr;
+constexpr int kStages = 4;                           // LDS ring of chunks
+constexpr int kRowBytes = 2 * (kDc + kDr);           // one cached token, bf16
+constexpr float kRescaleLog2 = 8.0f;                 // lazy-rescale threshold (2^8)
 
-struct MfmaParams {
-  const uint16_t* q_abs;
-  const uint16_t* q_rope;
-  const uint8_t* cache;
-  const int32_t* block_table;
-  const int32_t* seq_lens;
-  const int32_t* page_start;
-  float* o_part;
-  float* lse_part;
-  float c_log2;  // softmax scale * log2(e)
+struct MfmaParams {   // the scalar arguments of the kernel
+  int part_bf16;  // partials stored as bf16, else fp32
+  float c_log2;   // |softmax scale| * log2(e), at least FLT_MIN
+  int neg_q;      // the scale is negative: the kernel negates the queries (exact)
   int B, q_len, n_h, max_blocks, rows, row_groups;
   int64_t G;
 };
@@ -130,51 +136,57 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
 }
 
-// Per-lane source offsets of a page copy, precomputed once:
-//   content rows t = 16 j + 4 w + i (j, i in 0..3) need logical chunk
-//   lane ^ swz(t) of the row, and swz depends on t only through 4 w + i, so
-//   four patterns serve all 16 rows of the wave;
-//   rope rows are one per 8 lanes: row 8 (2 w + k) + lane / 8 of the page.
+// Per-lane source offsets of a chunk copy, precomputed once:
+//   content rows t = 16 j + 4 w + i (j in 0..1, i in 0..3) need logical
+//   16-byte unit lane ^ swz(t) of the row, and swz depends on t only through
+//   4 w + i, so four patterns serve all 8 rows of the wave;
+//   rope rows are one per 8 lanes: row 8 w + lane / 8 of the chunk.
 struct CopyPlan {
   uint32_t content[4];   // lane byte offset within a content row, per i
-  uint32_t rope[2];      // lane byte offset within the page, per rope group, all rows valid
+  uint32_t rope;         // lane byte offset within the chunk source, all rows valid
 };
 
-__device__ __forceinline__ uint32_t rope_src(int w, int k, int lane, int n_valid) {
-  const int t = 8 * (2 * w + k) + (lane >> 3);
+__device__ __forceinline__ uint32_t rope_src(int w, int lane, int n_valid) {
+  const int t = 8 * w + (lane >> 3);
   const int ts = t < n_valid ? t : 0;
   return ts * kRowBytes + 2 * kDc + (((lane & 7) ^ swz_rope(t)) << 4);
 }
 
-// Copy page `page` (tokens [0, n_valid) valid) into the LDS buffer at `buf`.
-// Rows past n_valid are read from row 0 so that every LDS value is finite.
-// `w` and `n_valid` are wave-uniform: all row arithmetic is scalar.
-__device__ __forceinline__ void load_tile(const uint8_t* cache, int64_t page, int n_valid,
-                                          uint32_t buf, int w, int lane, const CopyPlan& cp) {
-  const uint8_t* pg = cache + page * (64LL * kRowBytes);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * j + 4 * w + i;
-      const int ts = t < n_valid ? t : 0;
-      lds_dma16(pg + ts * kRowBytes, cp.content[i], buf + t * 1024);
-    }
-  if (n_valid == 64) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) lds_dma16(pg, cp.rope[k], buf + kContentBytes + (2 * w + k) * 1024);
+// Copy instruction i (0..8) of the 32-token chunk whose first cached row is
+// at `src` (tokens [0, n_valid) valid) into the LDS stage at `buf`:
+// instructions 0..7 copy content rows 16 (i / 4) + 4 w + i % 4, instruction 8
+// the wave's 8 rope rows. Rows past n_valid are read from row 0 so that every
+// LDS value is finite. `w` and `n_valid` are wave-uniform: all row
+// arithmetic is scalar.
+constexpr int kCopiesPerChunk = 9;
+__device__ __forceinline__ void copy_part(int i, const uint8_t* src, int n_valid, uint32_t buf,
+                                          int w, int lane, const CopyPlan& cp) {
+  if (i < 8) {
+    const int t = 16 * (i >> 2) + 4 * w + (i & 3);
+    const int ts = t < n_valid ? t : 0;
+    lds_dma16(src + ts * kRowBytes, cp.content[i & 3], buf + t * 1024);
   } else {
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      lds_dma16(pg, rope_src(w, k, lane, n_valid), buf + kContentBytes + (2 * w + k) * 1024);
+    lds_dma16(src, n_valid == kChunk ? cp.rope : rope_src(w, lane, n_valid),
+              buf + kChunkContent + w * 1024);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
-  // two page buffers: page `it` is computed from buffer it & 1 while page
-  // it + 1 is copied into the other
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kTileBytes];
-  __shared__ int restart_flag[2][4];   // per page parity, per wave
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding)
+#define MLA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+template <bool B>
+using bool_c = std::integral_constant<bool, B>;
+
+// Pointer arguments are separate restrict-qualified parameters, so that the
+// compiler reads the read-only tables with scalar loads.
+__global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
+    const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
+    const uint8_t* __restrict__ cache, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_start,
+    void* __restrict__ o_part, float* __restrict__ lse_part, MfmaParams p) {
+  // ring of chunk stages: chunk k lives in stage k % 4
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kChunkBytes];
+  __shared__ int restart_flag[4];   // per wave: some row raised its reference in this pass
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -182,13 +194,17 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
   CopyPlan cp;
 #pragma unroll
   for (int i = 0; i < 4; ++i) cp.content[i] = (lane ^ swz(4 * w + i)) << 4;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) cp.rope[k] = rope_src(w, k, lane, 64);
+  cp.rope = rope_src(w, lane, kChunk);
+
+  // block id -> (range, row group): ids congruent mod 8 run on one XCD; XCD x
+  // gets ranges [x G8, (x + 1) G8) with all their row groups
   const int64_t id = blockIdx.x;
-  const int rg = static_cast<int>((id >> 3) % p.row_groups);
-  const int64_t g = (id / (8LL * p.row_groups)) * 8 + (id & 7);
+  const int64_t G8 = (p.G + 7) / 8;
+  const int64_t jx = id >> 3;
+  const int64_t g = (id & 7) * G8 + jx / p.row_groups;
+  const int rg = static_cast<int>(jx % p.row_groups);
   if (g >= p.G) return;
-  const int64_t P = p.page_start[p.B];
+  const int64_t P = page_start[p.B];
   const int64_t pb = range_begin(g, P, p.G), pe = range_begin(g + 1, P, p.G);
   if (pb >= pe) return;
 
@@ -197,28 +213,29 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     int hi = p.B - 1;
     while (b < hi) {
       const int mid = (b + hi) >> 1;
-      if (p.page_start[mid + 1] > pb) hi = mid; else b = mid + 1;
+      if (page_start[mid + 1] > pb) hi = mid; else b = mid + 1;
     }
   }
 
   const int my_row = rg * kMfmaRows + w * 32 + l32;     // the row of this lane's columns
-  const int m = my_row / p.n_h, hd = my_row % p.n_h;
+  const int m = my_row / p.n_h;   // query token of this lane's row
   const float c = p.c_log2;
+  const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // LDS byte offsets of this lane's fragments. The swizzle only changes
-  // offset bits that the unrolled loop constants reach through an XOR, so one
-  // base register per pattern suffices: offset = (base ^ (k << s)) + imm.
+  // LDS byte offsets of this lane's fragments within a stage. The swizzle
+  // only changes offset bits that the unrolled loop constants reach through
+  // an XOR, so one base register per pattern suffices: offset = (base ^ k) + imm.
   const int hx = swz(l32);
-  // score A-fragment, token 32 ch + l32, content chunk 2 kc + half:
-  //   bits 5..7 = (kc & 7) ^ (hx >> 1), + 256 * (kc >> 3) + 32768 * ch
+  // score A-fragment, token l32, content unit 2 kc + half:
+  //   bits 5..7 = (kc & 7) ^ (hx >> 1), + 256 * (kc >> 3)
   const uint32_t qk_base = l32 * 1024 + ((half ^ (hx & 1)) << 4) + ((hx >> 1) << 5);
-  // rope chunk 2 kk + half of a 128-byte rope row: bits 5..6 = kk ^ (hr >> 1), + 4096 * ch
+  // rope unit 2 kk + half of a 128-byte rope row: bits 5..6 = kk ^ (hr >> 1)
   const int hr = swz_rope(l32);
-  const uint32_t rope_base = kContentBytes + l32 * 128 + ((half ^ (hr & 1)) << 4) + ((hr >> 1) << 5);
-  // transposed value reads: 16-lane group G16 = g16, source lane s16 reads
+  const uint32_t rope_base = kChunkContent + l32 * 128 + ((half ^ (hr & 1)) << 4) + ((hr >> 1) << 5);
+  // transposed value reads: 16-lane group g16, source lane s16 reads
   // row 4 (g16 >> 1) + (s16 >> 2) (+8 for the second read) of a 16-token
-  // chunk, columns 32 mb + 16 (g16 & 1) + 4 (s16 & 3):
-  //   bits 6..7 = (mb & 3) ^ (swz >> 2), + 256 * (mb >> 2) + 16384 * chunk
+  // step, columns 32 mb + 16 (g16 & 1) + 4 (s16 & 3):
+  //   bits 6..7 = (mb & 3) ^ (swz >> 2), + 256 * (mb >> 2) + 16384 * step
   const int g16 = lane >> 4, s16 = lane & 15;
   uint32_t pv_base[2];
 #pragma unroll
@@ -228,199 +245,323 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(MfmaParams p) {
     const int qlow = 2 * (g16 & 1) + ((s16 & 3) >> 1);
     pv_base[sec] = t * 1024 + ((qlow ^ (ht & 3)) << 4) + (s16 & 1) * 8 + ((ht >> 2) << 6);
   }
+  const uint32_t lds0 = lds_addr(smem);
 
-  for (; b < p.B && p.page_start[b] < pe; ++b) {
-    const int64_t s0 = p.page_start[b], s1 = p.page_start[b + 1];
+  for (; b < p.B && page_start[b] < pe; ++b) {
+    const int64_t s0 = page_start[b], s1 = page_start[b + 1];
     if (s1 == s0) continue;
     const int64_t a0 = s0 > pb ? s0 : pb, a1 = s1 < pe ? s1 : pe;
-    const int n_tiles = static_cast<int>(a1 - a0);
-    const int S = clamp_len(p.seq_lens[b], p.max_blocks);
+    const int n_pages = static_cast<int>(a1 - a0);
+    const int S = clamp_len(seq_lens[b], p.max_blocks);
     const int pidx0 = static_cast<int>(a0 - s0);
+    const int tok0 = pidx0 * 64;
     const int tok1 = min(S, static_cast<int>((a1 - s0) * 64));
+    const int n = (tok1 - tok0 + kChunk - 1) / kChunk;   // chunks of this piece (>= 1)
     const int tend = min(tok1, S - p.q_len + m + 1);      // this row's visible end
-    // tokens below tend_all are visible to every row of the wave
-    int tend_all = tend;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) tend_all = min(tend_all, __shfl_xor(tend_all, off, 64));
-    tend_all = __builtin_amdgcn_readfirstlane(tend_all);
-    const int32_t* bt = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
-    // page ids of this piece, 64 at a time: lane i holds page (base + i)
-    auto ids_at = [&](int first) {
-      const int k = pidx0 + first + lane;
-      return (first + lane < n_tiles && k < p.max_blocks) ? bt[k] : 0;
-    };
-    int ids_cur, ids_nxt;
-
-    // Q^T fragments: per 16-lane k chunk, the lane holds lanes [8 half, 8 half + 8) of its row
+    // tokens below tend_all are visible to every row of the wave (its first
+    // row has the smallest query index)
+    const int tend_all = min(tok1, S - p.q_len + (rg * kMfmaRows + w * 32) / p.n_h + 1);
+    const int32_t* bt = block_table + static_cast<int64_t>(b) * p.max_blocks;
+    // Q^T fragments: per 16-lane k unit, the lane holds lanes [8 half, 8 half + 8)
+    // of its row. The wave's 32 rows are consecutive (row b * rows + my_row),
+    // so the row base is scalar and each lane adds a 32-bit offset.
     bf16x8 qf[36];
-    {
-      const int64_t qrow = (static_cast<int64_t>(b) * p.q_len + m) * p.n_h + hd;
-      const bf16x8* qa = reinterpret_cast<const bf16x8*>(p.q_abs + qrow * kDc);
-      const bf16x8* qr = reinterpret_cast<const bf16x8*>(p.q_rope + qrow * kDr);
+    auto load_q = [&]() {
+      const int64_t qrow0 = static_cast<int64_t>(b) * p.rows + rg * kMfmaRows + w * 32;
+      const uint16_t* qa = q_abs + qrow0 * kDc;
+      const uint16_t* qr = q_rope + qrow0 * kDr;
 #pragma unroll
-      for (int kc = 0; kc < 32; ++kc) qf[kc] = qa[2 * kc + half];
+      for (int kc = 0; kc < 32; ++kc)
+        qf[kc] = *reinterpret_cast<const bf16x8*>(qa + l32 * kDc + 16 * kc + 8 * half);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qf[32 + kk] = qr[2 * kk + half];
-    }
+      for (int kk = 0; kk < 4; ++kk)
+        qf[32 + kk] = *reinterpret_cast<const bf16x8*>(qr + l32 * kDr + 16 * kk + 8 * half);
+    };
+    auto negate_q = [&]() {   // c s with c < 0 equals |c| (-s), and negating bf16 is exact
+#pragma unroll
+      for (int i = 0; i < 36; ++i) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        qf[i] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[i]) ^ 0x80008000u);
+      }
+    };
 
     f32x16 o[16];
     float m_run = -INFINITY, l_lane = 0.f;
-    const uint32_t lds0 = lds_addr(smem);
 
-    // The outer loop runs again only when a row's max rose past the lazy
-    // threshold: the piece restarts from its first page with the raised
-    // maxima (every wave sees the same flags, so all restart together).
-    for (bool again = true; again;) {
-      // zero O through the matrix unit: every definition of O is then an
-      // MFMA result, and the compiler keeps O in the accumulation registers
-      // across the page loop (a vector-ALU zero would make it carry O in the
-      // vector registers and copy it in and out on every page)
-      {
-        const bf16x8 z8 = {};
+
+    // zero O through the matrix unit: every definition of O is then an MFMA
+    // result, and the compiler keeps O in the accumulation registers across
+    // the chunk loop (a vector-ALU zero would make it carry O in the vector
+    // registers and copy it in and out on every chunk)
+    auto zero_o = [&]() {
+      const bf16x8 z8 = {};
 #pragma unroll
-        for (int mb = 0; mb < 16; ++mb)
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z8, z8, f32x16{}, 0, 0, 0);
-      }
+      for (int mb = 0; mb < 16; ++mb)
+        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z8, z8, f32x16{}, 0, 0, 0);
       l_lane = 0.f;
-      again = false;
-      ids_cur = ids_at(0);
-      ids_nxt = ids_at(64);
-      __syncthreads();   // earlier reads of both buffers are done
-      load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, 0), min(64, tok1 - pidx0 * 64), lds0, w,
-                lane, cp);
+    };
+    // first cached row of chunk q of the piece (the page id is a scalar load)
+    auto chunk_src = [&](int q) {
+      const int64_t page = bt[pidx0 + (q >> 1)];
+      return cache + page * (64LL * kRowBytes) + (q & 1) * (kChunk * kRowBytes);
+    };
+    auto chunk_valid = [&](int q) { return min(kChunk, tok1 - tok0 - kChunk * q); };
+    // copy all of chunk q into its stage at once
+    auto issue = [&](int q) {
+      const uint8_t* src = chunk_src(q);
+      const int nv = chunk_valid(q);
+#pragma unroll
+      for (int i = 0; i < kCopiesPerChunk; ++i)
+        copy_part(i, src, nv, lds0 + (q & 3) * kChunkBytes, w, lane, cp);
+    };
+    // first two chunks in flight; wait for chunk 0 everywhere
+    auto start = [&]() {
+      issue(0);
+      if (n > 1) issue(1);
+      if (n > 1) MLA_WAIT_VM(kCopiesPerChunk);
+      else MLA_WAIT_VM(0);
+    };
 
-      for (int it = 0;; ++it) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of page `it`
-        __syncthreads();                      // ... and every other wave's, and their flags
-        if (it > 0) {
-          const int* f = restart_flag[(it - 1) & 1];
-          if (f[0] | f[1] | f[2] | f[3]) {
-            again = true;
-            break;
+    float m_prev = 0.f;      // reference of the previous chunk's probabilities
+    f32x16 sp;               // raw (masked) scores of the previous chunk
+    auto clear_prev = [&]() {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sp[r] = -INFINITY;
+      m_prev = 0.f;
+    };
+    bool raise = false;      // some row of this lane crossed the lazy threshold in this pass
+
+    // One pipeline step k:
+    //   phase 1: scores of chunk k on the matrix unit, interleaved with the
+    //            exponentials of chunk k - 1 (p = 2^(c s - m)), their bf16
+    //            packing and their row sums, and with the copy of chunk k + 2
+    //            (one copy instruction every fourth MFMA);
+    //   mask:    only for a chunk that reaches past a row's visible end;
+    //   phase 2: weighted sum of chunk k - 1 on the matrix unit, interleaved
+    //            with the row max of chunk k and the lazy reference update.
+    // Every step runs the same code, so that one copy of the weighted sum
+    // keeps O in the accumulation registers: step 0 weighs chunk 0 with the
+    // zero probabilities of the empty chunk -1, and step n multiplies a stage
+    // whose scores the mask removes entirely.
+    auto step = [&](int k) {
+      const uint32_t bq = lds0 + (k & 3) * kChunkBytes;
+      const uint32_t bv = k == 0 ? bq : lds0 + ((k - 1) & 3) * kChunkBytes;
+      // stage (k + 2) % 4 last held chunk k - 2, whose weighted sum every
+      // wave finished before the barrier that opened this step
+      const bool copy = k + 2 < n;
+      const uint8_t* csrc = copy ? chunk_src(k + 2) : cache;
+      const int cnv = copy ? chunk_valid(k + 2) : kChunk;
+      const uint32_t cbuf = lds0 + ((k + 2) & 3) * kChunkBytes;
+      // the fragment bases pass through an empty asm statement, so that the
+      // per-fragment XOR variants are formed here, step by step, instead of
+      // being hoisted out of the loop (where they would pin 20 registers)
+      uint32_t qb = qk_base, rb = rope_base, vb0 = pv_base[0], vb1 = pv_base[1];
+      asm volatile("" : "+v"(qb), "+v"(rb), "+v"(vb0), "+v"(vb1));
+      const uint32_t qk_pg = bq + qb, rope_pg = bq + rb;
+      auto kfrag = [&](int kc) {
+        const uint32_t a = kc < 32 ? (qk_pg ^ ((kc & 7) << 5)) + (kc >> 3) * 256
+                                   : rope_pg ^ ((kc - 32) << 5);
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            static_cast<uintptr_t>(a));
+      };
+      const uint32_t pv0 = bv + vb0, pv1 = bv + vb1;
+      auto vfrag = [&](int st) {
+        const int mb = st & 15, cc = st >> 4;   // all column blocks of one 16-token step, then the next
+        const uint32_t off = (mb >> 2) * 256 + cc * 16384;
+        const s16x4 lo = lds_tr16a((pv0 ^ ((mb & 3) << 6)) + off);
+        const s16x4 hi = lds_tr16a((pv1 ^ ((mb & 3) << 6)) + off);
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      constexpr int kD = 4;   // score A-fragment read distance (MFMAs)
+      constexpr int kV = 4;   // value fragment read distance (MFMAs)
+      bf16x8 kf[kD + 1];
+      bf16x8 vf[kV + 1];
+      bf16x8 pf[2];
+
+      // exponentials of chunk k - 1: slot 2r computes p_r, the odd slots
+      // pack pairs to bf16 and add them to the row sum (the sum is taken
+      // over the bf16 weights the weighted sum uses). The empty asm
+      // statements pin each result to its slot: without them the optimizer
+      // sinks the whole softmax next to the weighted sum that consumes it,
+      // and the matrix unit idles while it runs.
+      auto smb_slot = [&](int s) {
+        const int r = s >> 1;
+        if (s < 32) {
+          if ((s & 1) == 0) {
+            sp[r] = __builtin_amdgcn_exp2f(fmaf(sp[r], c, -m_prev));
+            asm volatile("" : "+v"(sp[r]));
+          } else if (r & 1) {
+            const bf16x2 two = {static_cast<__bf16>(sp[r - 1]), static_cast<__bf16>(sp[r])};
+            pf[r >> 3][(r - 1) & 7] = two[0];
+            pf[r >> 3][r & 7] = two[1];
+            l_lane = __builtin_amdgcn_fdot2_f32_bf16(two, kOnes2, l_lane, false);
+            asm volatile("" : "+v"(l_lane));
           }
         }
-        if (it == n_tiles) break;
-        const uint32_t cur = (it & 1) * kTileBytes;
-        const uint32_t next = lds0 + (kTileBytes - cur);
-        // this page's fragment bases (cur only sets bits 13 and 16, which the
-        // XOR constants below never touch)
-        const uint32_t qk_pg = lds0 + cur + qk_base, rope_pg = lds0 + cur + rope_base;
-        const uint32_t pv_pg0 = lds0 + cur + pv_base[0], pv_pg1 = lds0 + cur + pv_base[1];
-        const int pidx = pidx0 + it;
-        if (it + 1 < n_tiles) {
-          if (((it + 1) & 63) == 0) {   // roll the page-id window
-            ids_cur = ids_nxt;
-            ids_nxt = ids_at(it + 65);
-          }
-          load_tile(p.cache, __builtin_amdgcn_readlane(ids_cur, (it + 1) & 63),
-                    min(64, tok1 - (pidx + 1) * 64), next, w, lane, cp);
-        }
-        bool raise = false;   // some row of this wave crossed the lazy threshold
+      };
 
+      // ---- phase 1: S^T = K Q^T of chunk k ----
+      f32x16 sn;
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          // ---- scores S^T = K Q^T for tokens [32 ch, 32 ch + 32) ----
-          // the per-half bases differ in the expression, so nothing is shared
-          // (and kept live) across the halves
-          const uint32_t qk_h = ch ? (qk_pg + 32768) : qk_pg;
-          const uint32_t rope_h = ch ? (rope_pg + 4096) : rope_pg;
-          auto kfrag = [&](int kc) {
-            const uint32_t a = kc < 32 ? (qk_h ^ ((kc & 7) << 5)) + (kc >> 3) * 256
-                                       : rope_h ^ ((kc - 32) << 5);
-            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                static_cast<uintptr_t>(a));
-          };
-          // A fragments are read kD steps ahead of their MFMAs; the
-          // scheduling barriers pin that order
-          constexpr int kD = 3;
-          bf16x8 kf[kD + 1];
+      for (int j = 0; j < kD; ++j) kf[j] = kfrag(j);
 #pragma unroll
-          for (int j = 0; j < kD; ++j) kf[j] = kfrag(j);
-          f32x16 sc;
-#pragma unroll
-          for (int kc = 0; kc < 36; ++kc) {
-            if (kc + kD < 36) kf[(kc + kD) % (kD + 1)] = kfrag(kc + kD);
-            if (kc == 0) mfma_s_first(sc, kf[0], qf[0]);
-            else if (kc == 35) mfma_s_last(sc, kf[kc % (kD + 1)], qf[kc]);
-            else mfma_s(sc, kf[kc % (kD + 1)], qf[kc]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int kc = 0; kc < 36; ++kc) {
+        if (kc + kD < 36) kf[(kc + kD) % (kD + 1)] = kfrag(kc + kD);
+        if (kc == 0) mfma_s_first(sn, kf[0], qf[0]);
+        else if (kc == 35) mfma_s_last(sn, kf[kc % (kD + 1)], qf[kc]);
+        else mfma_s(sn, kf[kc % (kD + 1)], qf[kc]);
+        smb_slot(kc);
+        if ((kc & 3) == 2 && copy) copy_part(kc >> 2, csrc, cnv, cbuf, w, lane, cp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
-          // ---- scale to log2 units, mask tokens at or past this row's end ----
-          float mx = -INFINITY;
-          if (pidx * 64 + 32 * ch + 32 <= tend_all) {   // wave-uniform: nothing to mask
+      // ---- mask tokens at or past the row's visible end (wave-uniform test) ----
+      if (tok0 + kChunk * k + kChunk > tend_all) {
+        const int lim = tend - (tok0 + kChunk * k) - 4 * half;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              sc[r] *= c;
-              mx = fmaxf(mx, sc[r]);
-            }
-          } else {
-            const int tk = pidx * 64 + 32 * ch + 4 * half;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              sc[r] = tk + (r & 3) + 8 * (r >> 2) < tend ? sc[r] * c : -INFINITY;
-              mx = fmaxf(mx, sc[r]);
-            }
-          }
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 16; ++r) sn[r] = (r & 3) + 8 * (r >> 2) < lim ? sn[r] : -INFINITY;
+      }
 
-          // ---- online softmax (base 2, lazy reference) ----
+      // ---- phase 2: row max of chunk k, reference update ----
+      float mx = -INFINITY;
+      auto sma_slot = [&](int s) {
+        if (s < 8) {
+          // max3 without the NaN canonicalisation that fmaxf adds (scores are
+          // finite or -inf)
+          asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(sn[2 * s]), "v"(sn[2 * s + 1]));
+          asm volatile("" : "+v"(mx));
+        } else if (s == 8) {   // the row's other 16 tokens sit in the other wave half
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+          asm volatile("" : "+v"(mx));
+        } else if (s == 9) {
           // rows that already hold weight and see a max above the lazy
           // threshold force a restart; the others just move their reference
-          if (mx > m_run + kRescaleLog2) {
-            if (m_run != -INFINITY) raise = true;
-            m_run = mx;
-          }
-          raise = __any(raise);
-          const float msub = m_run == -INFINITY ? 0.f : m_run;
-          bf16x8 pf[2];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(sc[r] - msub);
-            l_lane += pr;
-            pf[r >> 3][r & 7] = static_cast<__bf16>(pr);
-          }
-
-          // ---- weighted sum O^T += V^T P^T over these 32 tokens ----
-          const uint32_t pv_h0 = ch ? (pv_pg0 + 32768) : pv_pg0;
-          const uint32_t pv_h1 = ch ? (pv_pg1 + 32768) : pv_pg1;
-          auto vfrag = [&](int st) {
-            const int mb = st >> 1, cc = st & 1;
-            const uint32_t off = (mb >> 2) * 256 + cc * 16384;
-            const s16x4 lo = lds_tr16a((pv_h0 ^ ((mb & 3) << 6)) + off);
-            const s16x4 hi = lds_tr16a((pv_h1 ^ ((mb & 3) << 6)) + off);
-            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          };
-          constexpr int kV = 3;   // read distance in steps
-          bf16x8 vf[kV + 1];
-#pragma unroll
-          for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
-#pragma unroll
-          for (int st = 0; st < 32; ++st) {
-            if (st + kV < 32) vf[(st + kV) % (kV + 1)] = vfrag(st + kV);
-            o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % (kV + 1)], pf[st & 1],
-                                                                   o[st >> 1], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          const bool up = mx > m_run + kRescaleLog2;
+          raise = raise || (up && m_run != -INFINITY);
+          m_run = up ? mx : m_run;
         }
-        if (lane == 0) restart_flag[it & 1][w] = raise ? 1 : 0;
+      };
+      // ---- ... interleaved with O^T += V^T P^T over chunk k - 1 ----
+#pragma unroll
+      for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
+#pragma unroll
+      for (int st = 0; st < 32; ++st) {
+        if (st + kV < 32) vf[(st + kV) % (kV + 1)] = vfrag(st + kV);
+        o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % (kV + 1)], pf[st >> 4],
+                                                               o[st & 15], 0, 0, 0);
+        sma_slot(st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sp = sn;
+      m_prev = m_run == -INFINITY ? 0.f : m_run;
+    };
+
+    zero_o();
+    clear_prev();
+    __syncthreads();   // earlier reads of every stage are done
+    // chunk 0, the queries, chunk 1: waiting for all but chunk 1's copies
+    // then covers the queries too
+    issue(0);
+    load_q();
+    if (n > 1) {
+      issue(1);
+      MLA_WAIT_VM(kCopiesPerChunk);
+    } else {
+      MLA_WAIT_VM(0);
+    }
+    if (p.neg_q) negate_q();
+    // Chunk loop. A row whose max rose past the lazy threshold makes its wave
+    // raise a flag at the end of the pass; then the piece restarts in place
+    // from its first chunk with the raised maxima (every wave sees the same
+    // flags, so all restart together).
+    for (int k = 0; k <= n; ++k) {
+      if (k > 0 && k < n) {
+        if (k + 1 < n) MLA_WAIT_VM(kCopiesPerChunk);   // this wave's copies of chunk k
+        else MLA_WAIT_VM(0);
+      }
+      __syncthreads();     // ... and every other wave's
+      step(k);
+      if (k == n) {        // end of the pass: no copy is in flight
+        const bool any_raise = __any(raise);
+        if (lane == 0) restart_flag[w] = any_raise ? 1 : 0;
+        __syncthreads();
+        if (restart_flag[0] | restart_flag[1] | restart_flag[2] | restart_flag[3]) {
+          __syncthreads();   // every wave has read the flags
+          zero_o();
+          clear_prev();
+          raise = false;
+          start();
+          k = -1;
+        }
       }
     }
 
     // ---- epilogue: normalised partial and its log-sum-exp ----
+    // O^T sits in the MFMA layout (lane = row, registers = columns); the rows
+    // go through LDS so that each store instruction writes 1 KB of one row.
+    // LDS rows are padded to 1040 bytes, which spreads the 32 rows a write
+    // instruction touches over the banks, while every offset stays a
+    // compile-time immediate on one per-lane base.
     const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const int64_t slot = slot_of(g, b);
-    float* orow = p.o_part + (slot * p.rows + my_row) * static_cast<int64_t>(kDc);
+    constexpr int kEpiRow = 1040;
+    const uint32_t lrow = lds0 + (w * 32 + l32) * kEpiRow + 8 * half;
+    const uint32_t lrd = lds0 + w * 32 * kEpiRow + 16 * lane;
+    __syncthreads();                           // every wave is done with the stages
+    if (p.part_bf16) {
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb)
+      for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = f32x4{o[mb][4 * j], o[mb][4 * j + 1], o[mb][4 * j + 2], o[mb][4 * j + 3]} * inv;
-        *reinterpret_cast<f32x4*>(orow + mb * 32 + 4 * half + 8 * j) = v;
+        for (int j = 0; j < 4; ++j) {
+          // columns 32 mb + 8 j + 4 half + (0..3): 16-byte unit 4 mb + j, bytes 8 half
+          const bf16x2 lo = {static_cast<__bf16>(o[mb][4 * j] * inv), static_cast<__bf16>(o[mb][4 * j + 1] * inv)};
+          const bf16x2 hi = {static_cast<__bf16>(o[mb][4 * j + 2] * inv), static_cast<__bf16>(o[mb][4 * j + 3] * inv)};
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+              static_cast<uintptr_t>(lrow + (4 * mb + j) * 16)) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+      uint16_t* dst = static_cast<uint16_t*>(o_part) +
+                      (slot * p.rows + rg * kMfmaRows + w * 32) * static_cast<int64_t>(kDc) + 8 * lane;
+#pragma unroll 8
+      for (int rr = 0; rr < 32; ++rr) {
+        const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            static_cast<uintptr_t>(lrd + rr * kEpiRow));
+        *reinterpret_cast<f32x4*>(dst + rr * kDc) = v;
       }
+    } else {
+      float* dst = static_cast<float*>(o_part) +
+                   (slot * p.rows + rg * kMfmaRows + w * 32) * static_cast<int64_t>(kDc) + 4 * lane;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {         // columns [256 hh, 256 hh + 256): 1 KB per row
+#pragma unroll
+        for (int mb = 8 * hh; mb < 8 * hh + 8; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // columns 32 mb + 8 j + 4 half + (0..3) - 256 hh: unit 2 (4 (mb - 8 hh) + j) + half
+            const f32x4 v = f32x4{o[mb][4 * j], o[mb][4 * j + 1], o[mb][4 * j + 2], o[mb][4 * j + 3]} * inv;
+            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(
+                lrow + 8 * half + (2 * (4 * (mb - 8 * hh) + j)) * 16)) = v;
+          }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll 8
+        for (int rr = 0; rr < 32; ++rr) {
+          const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+              static_cast<uintptr_t>(lrd + rr * kEpiRow));
+          *reinterpret_cast<f32x4*>(dst + rr * kDc + 256 * hh) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
     if (half == 0)
-      p.lse_part[slot * p.rows + my_row] =
+      lse_part[slot * p.rows + my_row] =
           l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
   }
 }
@@ -435,15 +576,12 @@ bool mfma_supports(const mla_decode_desc* d) {
 mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   const mla_decode_desc* d = a.d;
   MfmaParams p;
-  p.q_abs = static_cast<const uint16_t*>(a.q_abs);
-  p.q_rope = static_cast<const uint16_t*>(a.q_rope);
-  p.cache = static_cast<const uint8_t*>(a.cache);
-  p.block_table = a.block_table;
-  p.seq_lens = a.seq_lens;
-  p.page_start = a.page_start;
-  p.o_part = a.o_part;
-  p.lse_part = a.lse_part;
-  p.c_log2 = a.scale * 1.4426950408889634f;
+  p.part_bf16 = a.p->part_bf16;
+  // the kernel scales scores by a positive factor (masked scores are -inf,
+  // and -inf * 0 would be NaN); a zero scale becomes FLT_MIN, which leaves
+  // every finite score's exponential at exactly 1
+  p.c_log2 = fmaxf(fabsf(a.scale) * 1.4426950408889634f, 1.17549435e-38f);
+  p.neg_q = a.scale < 0.f ? 1 : 0;
   p.B = d->batch;
   p.q_len = d->q_len;
   p.n_h = d->n_heads;
@@ -453,7 +591,9 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.G = a.p->G;
   const int64_t g_pad = (a.p->G + 7) / 8 * 8;
   const dim3 grid(static_cast<unsigned>(g_pad * a.p->row_groups)), block(256);
-  hipLaunchKernelGGL(decode_mfma_bf16, grid, block, 0, st, p);
+  hipLaunchKernelGGL(decode_mfma_bf16, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
+                     static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
+                     a.block_table, a.seq_lens, a.page_start, a.o_part, a.lse_part, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
   return MLA_OK;

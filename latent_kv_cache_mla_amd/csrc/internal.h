@@ -25,6 +25,7 @@ struct DecodePlan {
   int row_groups;    // workgroups per range along the row dimension
   int64_t G;         // number of page ranges (partitions)
   int64_t slots;     // G + B partial slots
+  int part_bf16;     // partials stored as bf16 (MFMA path with a bf16 output), else fp32
   size_t plan_off, opart_off, lse_off, total;  // workspace layout (bytes)
 };
 
@@ -51,7 +52,7 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   const int32_t* page_start;
   float scale;
-  float* o_part;
+  void* o_part;      // bf16 or fp32, per DecodePlan::part_bf16
   float* lse_part;
   void* o_latent;
   float* lse_out;
