@@ -151,7 +151,8 @@ mla_status prepare(const mla_decode_desc* d, const void* q_abs, const void* q_ro
 }
 
 mla_status run_partial(const DecodeArgs& a, hipStream_t st) {
-  if (!a.d->plan_ready) {
+  const bool in_kernel = a.p->path == Path::Mfma && mfma_lds_plan(a.d);
+  if (!a.d->plan_ready && !in_kernel) {
     mla_status s = launch_plan(a.seq_lens, a.d->batch, a.d->max_blocks_per_seq,
                                const_cast<int32_t*>(a.page_start), st);
     if (s != MLA_OK) return s;

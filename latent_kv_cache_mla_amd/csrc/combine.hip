@@ -55,9 +55,10 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   }
 }
 
-// One wavefront per output row (sequence b, row r): the lanes first reduce
-// the row's per-range log-sum-exps, then each lane combines 8 consecutive
-// latent lanes over the ranges.
+// One wavefront per output row (sequence b, row r): lane j first computes the
+// weight exp(lse_j - LSE) of range j of the row's ranges (64 at a time), then
+// every lane combines 8 consecutive latent lanes over the ranges, with four
+// partial loads in flight.
 template <typename PT, int OT>  // partial element type, output dtype
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
@@ -74,8 +75,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int64_t s0 = page_start[b], s1 = page_start[b + 1];
   const int64_t out_row = pair * d_c;
 
-  // ranges [glo, ghi] hold the sequence's pages; with more ranges than pages
-  // some ranges are empty and wrote nothing
+  // ranges [glo, glo + n) hold the sequence's pages; with more ranges than
+  // pages some ranges are empty and wrote nothing (weight 0, never read)
   int64_t glo = 0, n = 0;
   if (s1 > s0) {
     glo = range_of_page(s0, P, G);
@@ -101,15 +102,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 
   for (int c0 = 8 * lane; c0 < d_c; c0 += 512) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (mx != -INFINITY) {
-      for (int64_t j = 0; j < n; ++j) {
-        const float l = lse_of(j);   // wave-uniform
-        if (l == -INFINITY) continue;
-        const float wgt = expf(l - mx) * inv;
-        float v[8];
-        load8(o_part + (slot_of(glo + j, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v);
+    for (int64_t j0 = 0; j0 < n && mx != -INFINITY; j0 += 64) {
+      float wj = 0.f;
+      if (j0 + lane < n) {
+        const float l = lse_of(j0 + lane);
+        wj = l == -INFINITY ? 0.f : expf(l - mx) * inv;
+      }
+      const int cnt = static_cast<int>(n - j0 < 64 ? n - j0 : 64);
+      for (int j = 0; j < cnt; j += 4) {
+        float wgt[4], v[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt, v[i], acc[i]);
+        for (int u = 0; u < 4; ++u) {
+          wgt[u] = j + u < cnt ? __shfl(wj, j + u, 64) : 0.f;   // uniform
+          if (wgt[u] != 0.f)
+            load8(o_part + (slot_of(glo + j0 + j + u, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (wgt[u] != 0.f)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
       }
     }
     if constexpr (OT == MLA_FP32) {

@@ -179,14 +179,22 @@ using bool_c = std::integral_constant<bool, B>;
 
 // Pointer arguments are separate restrict-qualified parameters, so that the
 // compiler reads the read-only tables with scalar loads.
+//
+// kLdsPlan: every workgroup forms the page prefix sums itself in LDS (batch
+// up to kMaxLdsBatch), and workgroup 0 also stores them for the combine;
+// otherwise they come from the plan kernel through page_start.
+constexpr int kMaxLdsBatch = 1024;
+template <bool kLdsPlan>
 __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
     const uint8_t* __restrict__ cache, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_start,
+    const int32_t* __restrict__ seq_lens, int32_t* __restrict__ page_start,
     void* __restrict__ o_part, float* __restrict__ lse_part, MfmaParams p) {
   // ring of chunk stages: chunk k lives in stage k % 4
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kChunkBytes];
   __shared__ int restart_flag[4];   // per wave: some row raised its reference in this pass
+  __shared__ int ps_lds[kLdsPlan ? kMaxLdsBatch + 1 : 1];
+  __shared__ int scan_tmp[kLdsPlan ? 256 : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -204,7 +212,42 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   const int64_t g = (id & 7) * G8 + jx / p.row_groups;
   const int rg = static_cast<int>(jx % p.row_groups);
   if (g >= p.G) return;
-  const int64_t P = page_start[p.B];
+  if constexpr (kLdsPlan) {
+    // page_start[b] = sum_{b' < b} ceil(S_b' / 64): four sequences per thread,
+    // then a scan over the 256 thread totals
+    const int t = threadIdx.x;
+    int cnt[4], local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = 4 * t + i;
+      cnt[i] = bb < p.B ? static_cast<int>(pages_of(clamp_len(seq_lens[bb], p.max_blocks))) : 0;
+      local += cnt[i];
+    }
+    scan_tmp[t] = local;
+    __syncthreads();
+#pragma unroll
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = t >= off ? scan_tmp[t - off] : 0;
+      __syncthreads();
+      scan_tmp[t] += v;
+      __syncthreads();
+    }
+    int run = scan_tmp[t] - local;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bb = 4 * t + i;
+      if (bb <= p.B) ps_lds[bb] = run;
+      run += cnt[i];
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int bb = t; bb <= p.B; bb += 256) page_start[bb] = ps_lds[bb];
+  }
+  auto PS = [&](int i) -> int64_t {
+    if constexpr (kLdsPlan) return ps_lds[i];
+    else return page_start[i];
+  };
+  const int64_t P = PS(p.B);
   const int64_t pb = range_begin(g, P, p.G), pe = range_begin(g + 1, P, p.G);
   if (pb >= pe) return;
 
@@ -213,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     int hi = p.B - 1;
     while (b < hi) {
       const int mid = (b + hi) >> 1;
-      if (page_start[mid + 1] > pb) hi = mid; else b = mid + 1;
+      if (PS(mid + 1) > pb) hi = mid; else b = mid + 1;
     }
   }
 
@@ -247,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   }
   const uint32_t lds0 = lds_addr(smem);
 
-  for (; b < p.B && page_start[b] < pe; ++b) {
-    const int64_t s0 = page_start[b], s1 = page_start[b + 1];
+  for (; b < p.B && PS(b) < pe; ++b) {
+    const int64_t s0 = PS(b), s1 = PS(b + 1);
     if (s1 == s0) continue;
     const int64_t a0 = s0 > pb ? s0 : pb, a1 = s1 < pe ? s1 : pe;
     const int n_pages = static_cast<int>(a1 - a0);
@@ -568,6 +611,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
 
 }  // namespace
 
+bool mfma_lds_plan(const mla_decode_desc* d) { return d->batch <= kMaxLdsBatch; }
+
 bool mfma_supports(const mla_decode_desc* d) {
   return d->d_c == kDc && d->d_rope == kDr && d->cache_dtype == MLA_BF16 &&
          d->q_dtype == MLA_BF16 && (static_cast<int64_t>(d->q_len) * d->n_heads) % kMfmaRows == 0;
@@ -591,9 +636,16 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.G = a.p->G;
   const int64_t g_pad = (a.p->G + 7) / 8 * 8;
   const dim3 grid(static_cast<unsigned>(g_pad * a.p->row_groups)), block(256);
-  hipLaunchKernelGGL(decode_mfma_bf16, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
-                     static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
-                     a.block_table, a.seq_lens, a.page_start, a.o_part, a.lse_part, p);
+  if (mfma_lds_plan(d))
+    hipLaunchKernelGGL(decode_mfma_bf16<true>, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
+                       static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
+                       a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start), a.o_part,
+                       a.lse_part, p);
+  else
+    hipLaunchKernelGGL(decode_mfma_bf16<false>, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
+                       static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
+                       a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start), a.o_part,
+                       a.lse_part, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
   return MLA_OK;

@@ -61,6 +61,9 @@ struct DecodeArgs {
 mla_status launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
 bool mfma_supports(const mla_decode_desc* d);
+// The MFMA kernel forms the page prefix sums itself (and stores them for the
+// combine), so no plan launch is needed.
+bool mfma_lds_plan(const mla_decode_desc* d);
 mla_status launch_combine(const DecodeArgs& a, hipStream_t st);
 
 // fp32 strided batched GEMM: Y[b][m][n] = sum_k A[b](m,k) * B[b](k,n)
