@@ -48,6 +48,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def settle(fn, seconds: float = 0.3):
+    """Run `fn` untimed for about `seconds` before the warm-up steps: the GPU
+    raises its clocks only under sustained load, and a few warm-up steps are
+    not enough for that (the timed steps then mix two clock levels)."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def workload_sizes(cfg, seq_lens):
     import numpy as np
     bpt = {"bf16": 2 * cfg.lanes, "fp32": 4 * cfg.lanes, "fp8": cfg.d_c + 2 * cfg.d_rope + 4}[cfg.cache_dtype]
@@ -133,6 +147,7 @@ def main():
         mla.mla_decode(desc, qas[k], qrs[k], caches[k], dev["cache_scale"], dev["block_table"],
                        dev["seq_lens"], scale, outs[k], None, ws)
 
+    settle(step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -154,6 +169,7 @@ def main():
         mla.mla_decode_partial(pdesc, qas[k], qrs[k], caches[k], dev["cache_scale"],
                                dev["block_table"], dev["seq_lens"], scale, ws)
 
+    settle(part)
     for i in range(args.warmup):
         part(i)
     torch.cuda.synchronize()

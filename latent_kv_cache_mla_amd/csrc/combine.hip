@@ -55,10 +55,10 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   }
 }
 
-// One wavefront per output row (sequence b, row r): lane j first computes the
-// weight exp(lse_j - LSE) of range j of the row's ranges (64 at a time), then
-// every lane combines 8 consecutive latent lanes over the ranges, with four
-// partial loads in flight.
+// One wavefront per output row (sequence b, row r): lane j loads the
+// log-sum-exp of range j of the row's ranges (64 at a time) and forms its
+// weight exp(lse_j - LSE); then every lane combines 8 consecutive latent
+// lanes over the ranges, with eight partial loads in flight.
 template <typename PT, int OT>  // partial element type, output dtype
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
@@ -88,37 +88,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (may_be_empty && range_begin(g + 1, P, G) == range_begin(g, P, G)) return -INFINITY;
     return lse_part[slot_of(g, b) * rows + r];
   };
-  float mx = -INFINITY;
-  for (int64_t j = lane; j < n; j += 64) mx = fmaxf(mx, lse_of(j));
+  // lane j holds the log-sum-exp of range j (up to 64 ranges in registers;
+  // rows with more ranges reload them per block of 64)
+  float l0 = n > 0 && lane < n ? lse_of(lane) : -INFINITY;
+  float mx = l0;
+  for (int64_t j = lane + 64; j < n; j += 64) mx = fmaxf(mx, lse_of(j));
   mx = wave_max(mx);
   float wsum = 0.f;
-  if (mx != -INFINITY)
-    for (int64_t j = lane; j < n; j += 64) {
+  if (mx != -INFINITY) {
+    wsum = l0 == -INFINITY ? 0.f : expf(l0 - mx);
+    for (int64_t j = lane + 64; j < n; j += 64) {
       const float l = lse_of(j);
       if (l != -INFINITY) wsum += expf(l - mx);
     }
+  }
   wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
   for (int c0 = 8 * lane; c0 < d_c; c0 += 512) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t j0 = 0; j0 < n && mx != -INFINITY; j0 += 64) {
-      float wj = 0.f;
-      if (j0 + lane < n) {
-        const float l = lse_of(j0 + lane);
-        wj = l == -INFINITY ? 0.f : expf(l - mx) * inv;
-      }
+      float lj = l0;
+      if (j0 > 0) lj = j0 + lane < n ? lse_of(j0 + lane) : -INFINITY;
+      const float wj = lj == -INFINITY ? 0.f : expf(lj - mx) * inv;
       const int cnt = static_cast<int>(n - j0 < 64 ? n - j0 : 64);
-      for (int j = 0; j < cnt; j += 4) {
-        float wgt[4], v[4][8];
+      for (int j = 0; j < cnt; j += 8) {
+        float wgt[8], v[8][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
           wgt[u] = j + u < cnt ? __shfl(wj, j + u, 64) : 0.f;   // uniform
           if (wgt[u] != 0.f)
             load8(o_part + (slot_of(glo + j0 + j + u, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v[u]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 8; ++u)
           if (wgt[u] != 0.f)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
