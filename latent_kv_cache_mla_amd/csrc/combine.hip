@@ -55,20 +55,27 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
   }
 }
 
-// One wavefront per output row (sequence b, row r): lane j loads the
-// log-sum-exp of range j of the row's ranges (64 at a time) and forms its
-// weight exp(lse_j - LSE); then every lane combines 8 consecutive latent
-// lanes over the ranges, with eight partial loads in flight.
-template <typename PT, int OT>  // partial element type, output dtype
+// kWR wavefronts per output row (sequence b, row r); with kWR = 1 a block
+// holds four rows. Lane j of every wavefront loads the log-sum-exp of range j
+// of the row's ranges (64 at a time) and forms its weight exp(lse_j - LSE);
+// wavefront q then combines 8 consecutive latent lanes per lane over ranges
+// q, q + kWR, ..., with eight partial loads in flight, and the kWR partial
+// sums are added through LDS. Several wavefronts per row serve sequences cut
+// into many ranges (long contexts with a small batch).
+template <typename PT, int OT, int kWR>  // partial element type, output dtype, waves per row
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       void* __restrict__ o_latent,
                                                       float* __restrict__ lse_out,
                                                       int B, int rows, int d_c, int64_t G) {
+  static_assert(kWR == 1 || kWR == 2 || kWR == 4, "waves per row");
+  __shared__ float red[kWR > 1 ? 4 : 1][kWR > 1 ? 64 * 8 : 1];   // per wavefront of the block
   const int lane = threadIdx.x & 63;
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= static_cast<int64_t>(B) * rows) return;
+  const int wv = static_cast<int>(threadIdx.x >> 6);
+  const int q = wv % kWR;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (4 / kWR) + (threadIdx.x >> 6) / kWR;
+  if (pair >= static_cast<int64_t>(B) * rows) return;   // uniform per row's wavefronts
   const int64_t b = pair / rows;
   const int r = static_cast<int>(pair % rows);
   const int64_t P = page_start[B];
@@ -105,28 +112,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
-  for (int c0 = 8 * lane; c0 < d_c; c0 += 512) {
+  // the column loop is uniform across the block (barriers inside)
+  for (int cb = 0; cb < d_c; cb += 512) {
+    const int c0 = cb + 8 * lane;
+    const bool act = c0 < d_c;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t j0 = 0; j0 < n && mx != -INFINITY; j0 += 64) {
       float lj = l0;
       if (j0 > 0) lj = j0 + lane < n ? lse_of(j0 + lane) : -INFINITY;
       const float wj = lj == -INFINITY ? 0.f : expf(lj - mx) * inv;
       const int cnt = static_cast<int>(n - j0 < 64 ? n - j0 : 64);
-      for (int j = 0; j < cnt; j += 8) {
+      for (int j = q; j < cnt; j += 8 * kWR) {
         float wgt[8], v[8][8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          wgt[u] = j + u < cnt ? __shfl(wj, j + u, 64) : 0.f;   // uniform
-          if (wgt[u] != 0.f)
-            load8(o_part + (slot_of(glo + j0 + j + u, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v[u]);
+          const int jj = j + u * kWR;
+          wgt[u] = jj < cnt ? __shfl(wj, jj, 64) : 0.f;   // uniform
+          if (wgt[u] != 0.f && act)
+            load8(o_part + (slot_of(glo + j0 + jj, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v[u]);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (wgt[u] != 0.f)
+          if (wgt[u] != 0.f && act)
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
       }
     }
+    if constexpr (kWR > 1) {
+      __syncthreads();   // an earlier column block's sums have been read
+#pragma unroll
+      for (int i = 0; i < 8; ++i) red[wv][lane * 8 + i] = acc[i];
+      __syncthreads();
+      if (q != 0) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        for (int qq = 1; qq < kWR; ++qq) acc[i] += red[wv + qq][lane * 8 + i];
+    }
+    if (!act) continue;
     if constexpr (OT == MLA_FP32) {
       float* o = static_cast<float*>(o_latent) + out_row + c0;
       *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -140,7 +162,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
           make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
-  if (lse_out != nullptr && lane == 0) lse_out[pair] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+  if (lse_out != nullptr && lane == 0 && q == 0)
+    lse_out[pair] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 }  // namespace
@@ -153,27 +176,35 @@ mla_status launch_plan(const int32_t* seq_lens, int B, int max_blocks, int32_t* 
   return MLA_OK;
 }
 
-mla_status launch_combine(const DecodeArgs& a, hipStream_t st) {
+template <typename PT, int OT>
+void launch_combine_t(const DecodeArgs& a, const PT* op, hipStream_t st) {
   const int B = a.d->batch, rows = a.p->rows;
   const int64_t pairs = static_cast<int64_t>(B) * rows;
-  const dim3 grid(static_cast<unsigned>((pairs + 3) / 4)), block(256);
+  // ranges per sequence on average: more wavefronts per row when there are many
+  const int64_t per_seq = (a.p->G + B - 1) / B + 1;
+  const int wr = per_seq > 16 ? 4 : per_seq > 8 ? 2 : 1;
+  const dim3 block(256), grid(static_cast<unsigned>((pairs * wr + 3) / 4));
+  if (wr == 4)
+    hipLaunchKernelGGL((combine_kernel<PT, OT, 4>), grid, block, 0, st, a.page_start, op, a.lse_part,
+                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+  else if (wr == 2)
+    hipLaunchKernelGGL((combine_kernel<PT, OT, 2>), grid, block, 0, st, a.page_start, op, a.lse_part,
+                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+  else
+    hipLaunchKernelGGL((combine_kernel<PT, OT, 1>), grid, block, 0, st, a.page_start, op, a.lse_part,
+                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+}
+
+mla_status launch_combine(const DecodeArgs& a, hipStream_t st) {
   const bool bf16_out = a.d->out_dtype == MLA_BF16;
   if (a.p->part_bf16) {
     const uint16_t* op = static_cast<const uint16_t*>(a.o_part);
-    if (bf16_out)
-      hipLaunchKernelGGL((combine_kernel<uint16_t, MLA_BF16>), grid, block, 0, st, a.page_start, op,
-                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
-    else
-      hipLaunchKernelGGL((combine_kernel<uint16_t, MLA_FP32>), grid, block, 0, st, a.page_start, op,
-                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+    if (bf16_out) launch_combine_t<uint16_t, MLA_BF16>(a, op, st);
+    else launch_combine_t<uint16_t, MLA_FP32>(a, op, st);
   } else {
     const float* op = static_cast<const float*>(a.o_part);
-    if (bf16_out)
-      hipLaunchKernelGGL((combine_kernel<float, MLA_BF16>), grid, block, 0, st, a.page_start, op,
-                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
-    else
-      hipLaunchKernelGGL((combine_kernel<float, MLA_FP32>), grid, block, 0, st, a.page_start, op,
-                         a.lse_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+    if (bf16_out) launch_combine_t<float, MLA_BF16>(a, op, st);
+    else launch_combine_t<float, MLA_FP32>(a, op, st);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
