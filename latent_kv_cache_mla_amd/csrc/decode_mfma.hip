@@ -74,7 +74,17 @@ constexpr int kDr = 64;
 constexpr int kChunk = 32;                           // tokens per pipeline stage
 constexpr int kChunkContent = kChunk * 2 * kDc;      // 32 tokens x 512 bf16
 constexpr int kChunkBytes = kChunkContent + kChunk * 2 * kDr;
-constexpr int kStages = 4;                           // LDS ring of chunks
+constexpr int kStages = 4;                           // LDS ring of chunks (bf16 cache)
+// fp8 cache: rows of 512 e4m3 codes and 64 bf16 rope lanes, plus one fp32
+// scale per token. Chunks land in one of two staging buffers and are then
+// dequantised into a ring of three bf16 stages laid out exactly like the bf16
+// cache's, so scores, softmax and weighted sum are shared.
+constexpr int kF8Row = kDc + 2 * kDr;                // 640 bytes per cached token
+constexpr int kF8Codes = kChunk * kDc;               // 16 KB of codes per chunk
+constexpr int kF8Rope = kChunk * 2 * kDr;            // 4 KB of rope lanes per chunk
+constexpr int kF8Stage = kF8Codes + kF8Rope + kChunk * 4;
+constexpr int kF8Stages = 3;
+constexpr int kF8CopiesPerChunk = 6;
 constexpr int kRowBytes = 2 * (kDc + kDr);           // one cached token, bf16
 constexpr float kRescaleLog2 = 8.0f;                 // lazy-rescale threshold (2^8)
 
@@ -171,8 +181,29 @@ __device__ __forceinline__ void copy_part(int i, const uint8_t* src, int n_valid
   }
 }
 
-// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding)
-#define MLA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+// Copy instruction i (0..5) of an fp8 chunk: the 32 code rows (two tokens per
+// instruction, instructions 0..3), the wave's 8 rope rows (4) and the wave's 8
+// scales (5, two lanes). `src` is the chunk's first cached row, `ssrc` its
+// first scale; rows past n_valid are read from row 0.
+__device__ __forceinline__ void copy_part_f8(int i, const uint8_t* src, const uint8_t* ssrc,
+                                             int n_valid, uint32_t stg, int w, int lane) {
+  if (i < 4) {
+    const int j = 4 * w + i;                  // token pair
+    const int t = 2 * j + (lane >> 5);
+    const int ts = t < n_valid ? t : 0;
+    lds_dma16(src, ts * kF8Row + (lane & 31) * 16, stg + j * 1024);
+  } else if (i == 4) {
+    const int t = 8 * w + (lane >> 3);
+    const int ts = t < n_valid ? t : 0;
+    lds_dma16(src, ts * kF8Row + kDc + (lane & 7) * 16, stg + kF8Codes + w * 1024);
+  } else if (lane < 2) {
+    lds_dma16(ssrc, (8 * w + 4 * lane) * 4, stg + kF8Codes + kF8Rope + w * 32);
+  }
+}
+
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+#define MLA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
@@ -184,14 +215,17 @@ using bool_c = std::integral_constant<bool, B>;
 // up to kMaxLdsBatch), and workgroup 0 also stores them for the combine;
 // otherwise they come from the plan kernel through page_start.
 constexpr int kMaxLdsBatch = 1024;
-template <bool kLdsPlan>
+template <bool kLdsPlan, bool kFp8>
 __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
-    const uint8_t* __restrict__ cache, const int32_t* __restrict__ block_table,
-    const int32_t* __restrict__ seq_lens, int32_t* __restrict__ page_start,
-    void* __restrict__ o_part, float* __restrict__ lse_part, MfmaParams p) {
-  // ring of chunk stages: chunk k lives in stage k % 4
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kChunkBytes];
+    const uint8_t* __restrict__ cache, const float* __restrict__ cache_scale,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
+    int32_t* __restrict__ page_start, void* __restrict__ o_part, float* __restrict__ lse_part,
+    MfmaParams p) {
+  // ring of bf16 chunk stages: chunk k lives in stage k % kS (fp8: plus two
+  // staging buffers after the ring)
+  constexpr int kS = kFp8 ? kF8Stages : kStages;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kS * kChunkBytes + (kFp8 ? 2 * kF8Stage : 0)];
   __shared__ int restart_flag[4];   // per wave: some row raised its reference in this pass
   __shared__ int ps_lds[kLdsPlan ? kMaxLdsBatch + 1 : 1];
   __shared__ int scan_tmp[kLdsPlan ? 256 : 1];
@@ -344,25 +378,87 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       l_lane = 0.f;
     };
     // first cached row of chunk q of the piece (the page id is a scalar load)
+    constexpr int kRow = kFp8 ? kF8Row : kRowBytes;
+    auto chunk_page = [&](int q) -> int64_t { return bt[pidx0 + (q >> 1)]; };
     auto chunk_src = [&](int q) {
-      const int64_t page = bt[pidx0 + (q >> 1)];
-      return cache + page * (64LL * kRowBytes) + (q & 1) * (kChunk * kRowBytes);
+      return cache + chunk_page(q) * (64LL * kRow) + (q & 1) * (kChunk * kRow);
     };
     auto chunk_valid = [&](int q) { return min(kChunk, tok1 - tok0 - kChunk * q); };
-    // copy all of chunk q into its stage at once
+    auto stage_of = [&](int q) { return lds0 + static_cast<uint32_t>(q % kS) * kChunkBytes; };
+    const uint32_t stg0 = lds0 + kS * kChunkBytes;   // fp8 staging buffers
+    // copy all of chunk q at once (into its stage, or for fp8 its staging buffer)
     auto issue = [&](int q) {
       const uint8_t* src = chunk_src(q);
       const int nv = chunk_valid(q);
+      if constexpr (kFp8) {
+        const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
+            cache_scale + chunk_page(q) * 64 + (q & 1) * kChunk);
 #pragma unroll
-      for (int i = 0; i < kCopiesPerChunk; ++i)
-        copy_part(i, src, nv, lds0 + (q & 3) * kChunkBytes, w, lane, cp);
+        for (int i = 0; i < kF8CopiesPerChunk; ++i)
+          copy_part_f8(i, src, ssrc, nv, stg0 + (q & 1) * kF8Stage, w, lane);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kCopiesPerChunk; ++i)
+          copy_part(i, src, nv, stage_of(q), w, lane, cp);
+      }
     };
-    // first two chunks in flight; wait for chunk 0 everywhere
+    // fp8: dequantise chunk q from its staging buffer into its bf16 stage:
+    // thread (token t, group g) turns codes [64 g, 64 g + 64) of row t into
+    // bf16 (e4m3 decoded exactly, times the token's scale, rounded to bf16)
+    // and copies 16 bytes of the rope row; rows past the valid tokens get
+    // scale 0. Every wave must have waited for the copies (and passed a
+    // barrier) before, and a barrier must follow before the stage is read.
+    auto dequant = [&](int q) {
+      const int t = threadIdx.x >> 3, gq = threadIdx.x & 7;
+      const uint32_t sb = stg0 + (q & 1) * kF8Stage;
+      const uint32_t db = stage_of(q);
+      const float sc = t < chunk_valid(q)
+                           ? *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+                                 static_cast<uintptr_t>(sb + kF8Codes + kF8Rope + 4 * t))
+                           : 0.f;
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const int hs = swz(t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 c4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            static_cast<uintptr_t>(sb + t * kDc + gq * 64 + i * 16));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {      // 8 codes -> one 16-byte bf16 unit
+          u32x4 o4;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t wd = c4[2 * h + e];
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wd), false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wd), true);
+            const bf16x2 b0 = {static_cast<__bf16>(lo[0] * sc), static_cast<__bf16>(lo[1] * sc)};
+            const bf16x2 b1 = {static_cast<__bf16>(hi[0] * sc), static_cast<__bf16>(hi[1] * sc)};
+            o4[2 * e] = __builtin_bit_cast(uint32_t, b0);
+            o4[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
+          }
+          const int unit = 8 * gq + 2 * i + h;
+          *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+              static_cast<uintptr_t>(db + t * 1024 + ((unit ^ hs) << 4))) = o4;
+        }
+      }
+      const u32x4 r4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          static_cast<uintptr_t>(sb + kF8Codes + t * 128 + gq * 16));
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(static_cast<uintptr_t>(
+          db + kChunkContent + t * 128 + ((gq ^ swz_rope(t)) << 4))) = r4;
+    };
+    // first two chunks in flight; wait for chunk 0 everywhere (fp8: and
+    // dequantise it)
     auto start = [&]() {
       issue(0);
       if (n > 1) issue(1);
-      if (n > 1) MLA_WAIT_VM(kCopiesPerChunk);
-      else MLA_WAIT_VM(0);
+      if constexpr (kFp8) {
+        if (n > 1) MLA_WAIT_VM(kF8CopiesPerChunk);
+        else MLA_WAIT_VM(0);
+        __syncthreads();
+        dequant(0);
+      } else {
+        if (n > 1) MLA_WAIT_VM(kCopiesPerChunk);
+        else MLA_WAIT_VM(0);
+      }
     };
 
     float m_prev = 0.f;      // reference of the previous chunk's probabilities
@@ -387,14 +483,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // zero probabilities of the empty chunk -1, and step n multiplies a stage
     // whose scores the mask removes entirely.
     auto step = [&](int k) {
-      const uint32_t bq = lds0 + (k & 3) * kChunkBytes;
-      const uint32_t bv = k == 0 ? bq : lds0 + ((k - 1) & 3) * kChunkBytes;
+      const uint32_t bq = stage_of(k);
+      const uint32_t bv = k == 0 ? bq : stage_of(k + kS - 1);
       // stage (k + 2) % 4 last held chunk k - 2, whose weighted sum every
-      // wave finished before the barrier that opened this step
-      const bool copy = k + 2 < n;
+      // wave finished before the barrier that opened this step (the fp8 path
+      // copies outside the step)
+      const bool copy = !kFp8 && k + 2 < n;
       const uint8_t* csrc = copy ? chunk_src(k + 2) : cache;
       const int cnv = copy ? chunk_valid(k + 2) : kChunk;
-      const uint32_t cbuf = lds0 + ((k + 2) & 3) * kChunkBytes;
+      const uint32_t cbuf = stage_of(k + 2);
       // the fragment bases pass through an empty asm statement, so that the
       // per-fragment XOR variants are formed here, step by step, instead of
       // being hoisted out of the loop (where they would pin 20 registers)
@@ -504,15 +601,28 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     zero_o();
     clear_prev();
     __syncthreads();   // earlier reads of every stage are done
-    // chunk 0, the queries, chunk 1: waiting for all but chunk 1's copies
-    // then covers the queries too
-    issue(0);
-    load_q();
-    if (n > 1) {
-      issue(1);
-      MLA_WAIT_VM(kCopiesPerChunk);
-    } else {
+    if constexpr (kFp8) {
+      // chunks 0 and 1, then the queries: chunk 0 is dequantised while the
+      // queries are still in flight
+      issue(0);
+      if (n > 1) issue(1);
+      load_q();
+      if (n > 1) MLA_WAIT_VM(kF8CopiesPerChunk + 36);
+      else MLA_WAIT_VM(36);
+      __syncthreads();
+      dequant(0);
       MLA_WAIT_VM(0);
+    } else {
+      // chunk 0, the queries, chunk 1: waiting for all but chunk 1's copies
+      // then covers the queries too
+      issue(0);
+      load_q();
+      if (n > 1) {
+        issue(1);
+        MLA_WAIT_VM(kCopiesPerChunk);
+      } else {
+        MLA_WAIT_VM(0);
+      }
     }
     if (p.neg_q) negate_q();
     // Chunk loop. A row whose max rose past the lazy threshold makes its wave
@@ -520,11 +630,22 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // from its first chunk with the raised maxima (every wave sees the same
     // flags, so all restart together).
     for (int k = 0; k <= n; ++k) {
-      if (k > 0 && k < n) {
-        if (k + 1 < n) MLA_WAIT_VM(kCopiesPerChunk);   // this wave's copies of chunk k
-        else MLA_WAIT_VM(0);
+      if constexpr (kFp8) {
+        // chunk k was dequantised in the previous step (or the prologue);
+        // chunk k + 1 must have landed in its staging buffer
+        if (k + 1 < n) MLA_WAIT_VM(0);
+        __syncthreads();
+        // stage (k + 1) % 3 last held chunk k - 2 and staging buffer k % 2
+        // chunk k, both done with before the barrier
+        if (k + 1 < n) dequant(k + 1);
+        if (k + 2 < n) issue(k + 2);
+      } else {
+        if (k > 0 && k < n) {
+          if (k + 1 < n) MLA_WAIT_VM(kCopiesPerChunk);   // this wave's copies of chunk k
+          else MLA_WAIT_VM(0);
+        }
+        __syncthreads();     // ... and every other wave's
       }
-      __syncthreads();     // ... and every other wave's
       step(k);
       if (k == n) {        // end of the pass: no copy is in flight
         const bool any_raise = __any(raise);
@@ -614,7 +735,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
 bool mfma_lds_plan(const mla_decode_desc* d) { return d->batch <= kMaxLdsBatch; }
 
 bool mfma_supports(const mla_decode_desc* d) {
-  return d->d_c == kDc && d->d_rope == kDr && d->cache_dtype == MLA_BF16 &&
+  return d->d_c == kDc && d->d_rope == kDr &&
+         (d->cache_dtype == MLA_BF16 || d->cache_dtype == MLA_FP8_E4M3) &&
          d->q_dtype == MLA_BF16 && (static_cast<int64_t>(d->q_len) * d->n_heads) % kMfmaRows == 0;
 }
 
@@ -636,16 +758,13 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.G = a.p->G;
   const int64_t g_pad = (a.p->G + 7) / 8 * 8;
   const dim3 grid(static_cast<unsigned>(g_pad * a.p->row_groups)), block(256);
-  if (mfma_lds_plan(d))
-    hipLaunchKernelGGL(decode_mfma_bf16<true>, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
-                       static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
-                       a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start), a.o_part,
-                       a.lse_part, p);
-  else
-    hipLaunchKernelGGL(decode_mfma_bf16<false>, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
-                       static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
-                       a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start), a.o_part,
-                       a.lse_part, p);
+  const bool lds_plan = mfma_lds_plan(d), fp8 = d->cache_dtype == MLA_FP8_E4M3;
+  auto kernel = lds_plan ? (fp8 ? decode_mfma_bf16<true, true> : decode_mfma_bf16<true, false>)
+                         : (fp8 ? decode_mfma_bf16<false, true> : decode_mfma_bf16<false, false>);
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
+                     static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
+                     a.cache_scale, a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start),
+                     a.o_part, a.lse_part, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
   return MLA_OK;
