@@ -445,6 +445,48 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(static_cast<uintptr_t>(
           db + kChunkContent + t * 128 + ((gq ^ swz_rope(t)) << 4))) = r4;
     };
+    // The same dequantisation in pieces, for the pipeline step: dq_load
+    // issues the LDS reads of the thread's 64 codes and its scale and copies
+    // the rope unit; dq_part(j), j = 0..15, converts 4 codes and stores a
+    // 16-byte unit after every second part.
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    u32x4_t dq_c[2], dq_o;   // codes of the current and the next 16-code group
+    float dq_s = 0.f;
+    auto dq_codes = [&](int q, int i, int tid) {
+      const int t = tid >> 3, gq = tid & 7;
+      dq_c[i & 1] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+          static_cast<uintptr_t>(stg0 + (q & 1) * kF8Stage + t * kDc + gq * 64 + i * 16));
+    };
+    auto dq_load = [&](int q, int tid) {
+      const int t = tid >> 3, gq = tid & 7;
+      const uint32_t sb = stg0 + (q & 1) * kF8Stage;
+      dq_codes(q, 0, tid);
+      dq_s = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
+          static_cast<uintptr_t>(sb + kF8Codes + kF8Rope + 4 * t));
+      if (t >= chunk_valid(q)) dq_s = 0.f;
+      const u32x4_t r4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+          static_cast<uintptr_t>(sb + kF8Codes + t * 128 + gq * 16));
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(
+          stage_of(q) + kChunkContent + t * 128 + ((gq ^ swz_rope(t)) << 4))) = r4;
+    };
+    auto dq_part = [&](int q, int j, int tid) {
+      const int t = tid >> 3, gq = tid & 7;
+      const int i = j >> 2, h = (j >> 1) & 1, e = j & 1;
+      if ((j & 3) == 0 && i < 3) dq_codes(q, i + 1, tid);   // one group ahead
+      const uint32_t wd = dq_c[i & 1][2 * h + e];
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wd), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wd), true);
+      const bf16x2 b0 = {static_cast<__bf16>(lo[0] * dq_s), static_cast<__bf16>(lo[1] * dq_s)};
+      const bf16x2 b1 = {static_cast<__bf16>(hi[0] * dq_s), static_cast<__bf16>(hi[1] * dq_s)};
+      dq_o[2 * e] = __builtin_bit_cast(uint32_t, b0);
+      dq_o[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
+      asm volatile("" : "+v"(dq_o));
+      if (e == 1) {
+        const int unit = 8 * gq + 2 * i + h;
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(
+            stage_of(q) + t * 1024 + ((unit ^ swz(t)) << 4))) = dq_o;
+      }
+    };
     // first two chunks in flight; wait for chunk 0 everywhere (fp8: and
     // dequantise it)
     auto start = [&]() {
@@ -488,15 +530,23 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       // stage (k + 2) % 4 last held chunk k - 2, whose weighted sum every
       // wave finished before the barrier that opened this step (the fp8 path
       // copies outside the step)
-      const bool copy = !kFp8 && k + 2 < n;
+      const bool copy = k + 2 < n;
       const uint8_t* csrc = copy ? chunk_src(k + 2) : cache;
       const int cnv = copy ? chunk_valid(k + 2) : kChunk;
       const uint32_t cbuf = stage_of(k + 2);
+      // fp8: the scale rows of chunk k + 2, and whether chunk k + 1 is to be
+      // dequantised in this step
+      const uint8_t* ssrc = kFp8 && copy ? reinterpret_cast<const uint8_t*>(
+          cache_scale + chunk_page(k + 2) * 64 + ((k + 2) & 1) * kChunk) : cache;
+      const bool dq = kFp8 && k + 1 < n;
       // the fragment bases pass through an empty asm statement, so that the
       // per-fragment XOR variants are formed here, step by step, instead of
       // being hoisted out of the loop (where they would pin 20 registers)
       uint32_t qb = qk_base, rb = rope_base, vb0 = pv_base[0], vb1 = pv_base[1];
       asm volatile("" : "+v"(qb), "+v"(rb), "+v"(vb0), "+v"(vb1));
+      // (fp8) the thread id, re-derived per step for the same reason
+      int tid_s = static_cast<int>(threadIdx.x);
+      if constexpr (kFp8) asm volatile("" : "+v"(tid_s));
       const uint32_t qk_pg = bq + qb, rope_pg = bq + rb;
       auto kfrag = [&](int kc) {
         const uint32_t a = kc < 32 ? (qk_pg ^ ((kc & 7) << 5)) + (kc >> 3) * 256
@@ -512,8 +562,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         const s16x4 hi = lds_tr16a((pv1 ^ ((mb & 3) << 6)) + off);
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      constexpr int kD = 4;   // score A-fragment read distance (MFMAs)
-      constexpr int kV = 4;   // value fragment read distance (MFMAs)
+      constexpr int kD = kFp8 ? 3 : 4;   // score A-fragment read distance (MFMAs)
+      constexpr int kV = kFp8 ? 3 : 4;   // value fragment read distance (MFMAs)
       bf16x8 kf[kD + 1];
       bf16x8 vf[kV + 1];
       bf16x8 pf[2];
@@ -551,7 +601,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         else if (kc == 35) mfma_s_last(sn, kf[kc % (kD + 1)], qf[kc]);
         else mfma_s(sn, kf[kc % (kD + 1)], qf[kc]);
         smb_slot(kc);
-        if ((kc & 3) == 2 && copy) copy_part(kc >> 2, csrc, cnv, cbuf, w, lane, cp);
+        if constexpr (kFp8) {
+          if ((kc & 3) == 2 && kc < 24 && copy)
+            copy_part_f8(kc >> 2, csrc, ssrc, cnv, stg0 + ((k + 2) & 1) * kF8Stage, w, tid_s & 63);
+        } else {
+          if ((kc & 3) == 2 && copy) copy_part(kc >> 2, csrc, cnv, cbuf, w, lane, cp);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -592,6 +647,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % (kV + 1)], pf[st >> 4],
                                                                o[st & 15], 0, 0, 0);
         sma_slot(st);
+        if constexpr (kFp8) {
+          if (dq) {
+            if (st == 0) dq_load(k + 1, tid_s);
+            else if (st >= 10 && st < 26) dq_part(k + 1, st - 10, tid_s);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       sp = sn;
@@ -635,10 +696,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         // chunk k + 1 must have landed in its staging buffer
         if (k + 1 < n) MLA_WAIT_VM(0);
         __syncthreads();
-        // stage (k + 1) % 3 last held chunk k - 2 and staging buffer k % 2
-        // chunk k, both done with before the barrier
-        if (k + 1 < n) dequant(k + 1);
-        if (k + 2 < n) issue(k + 2);
+        // the step dequantises chunk k + 1 into stage (k + 1) % 3 (which last
+        // held chunk k - 2) and copies chunk k + 2 into staging buffer k % 2
+        // (which held chunk k): both were done with before the barrier
       } else {
         if (k > 0 && k < n) {
           if (k + 1 < n) MLA_WAIT_VM(kCopiesPerChunk);   // this wave's copies of chunk k
