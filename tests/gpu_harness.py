@@ -58,8 +58,9 @@ def device_inputs(inp: wl.DecodeInputs, max_blocks: int | None = None):
 
 
 def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: bool = True,
-               plan_separately: bool = False, with_lse: bool = True):
-    """Runs mla_decode on the GPU; returns (o float64 [B,q_len,n_h,d_c], lse)."""
+               plan_separately: bool = False, with_lse: bool = True, scale: float | None = None):
+    """Runs mla_decode on the GPU; returns (o float64 [B,q_len,n_h,d_c], lse).
+    `scale` overrides the config's softmax scale."""
     m = lib()
     cfg = inp.cfg
     dev = dev or device_inputs(inp)
@@ -81,7 +82,8 @@ def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: 
         m.mla_decode_plan(desc, dev["seq_lens"], ws)
         desc.plan_ready = 1
     m.mla_decode(desc, dev["q_abs"], dev["q_rope"], dev["cache"], dev["cache_scale"],
-                 dev["block_table"], dev["seq_lens"], cfg.softmax_scale, o, lse, ws)
+                 dev["block_table"], dev["seq_lens"],
+                 cfg.softmax_scale if scale is None else scale, o, lse, ws)
     torch.cuda.synchronize()
     o64 = o.float().cpu().numpy().astype(np.float64)
     lse64 = None if lse is None else lse.cpu().numpy().astype(np.float64)
@@ -107,7 +109,7 @@ def oracle_queries(inp: wl.DecodeInputs):
     return oracle.bf16_bits_to_f64(inp.q_abs_bits), oracle.bf16_bits_to_f64(inp.q_rope_bits)
 
 
-def oracle_decode(inp: wl.DecodeInputs, batches=None):
+def oracle_decode(inp: wl.DecodeInputs, batches=None, scale: float | None = None):
     """Oracle output for all (or some) sequences: (o, lse) float64."""
     cfg = inp.cfg
     qa, qr = oracle_queries(inp)
@@ -116,7 +118,8 @@ def oracle_decode(inp: wl.DecodeInputs, batches=None):
     lse = np.zeros((len(idx), cfg.q_len, cfg.n_heads))
     for k, b in enumerate(idx):
         c, kr = oracle_inputs(inp, b)
-        r = oracle.latent_attention(qa[b], qr[b], c, kr, cfg.softmax_scale)
+        r = oracle.latent_attention(qa[b], qr[b], c, kr,
+                                    cfg.softmax_scale if scale is None else scale)
         o[k], lse[k] = r["o"], r["lse"]
     return o, lse
 

@@ -191,3 +191,31 @@ def test_validate_catches_bad_contents():
     long = torch.tensor([130, 64 * dev["max_blocks"] + 1], dtype=torch.int32, device="cuda")
     with pytest.raises(m.MlaError):
         m.mla_decode_validate(desc, long, dev["block_table"], dev["n_pages"])
+
+
+def test_batch_above_the_in_kernel_prefix_limit():
+    """More than 1024 sequences: the matrix-core kernel reads the page prefix
+    sums the plan kernel wrote instead of forming them itself."""
+    cfg = wl.scaled(C["c4"], batch=1100, ragged=(1, 130))
+    H.say(f"case large batch B={cfg.batch} lens={cfg.ragged} (plan kernel path)")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    pick = sorted({0, 1, 2, 511, 1023, 1024, 1025, 1098, 1099} | set(range(100, 1100, 97)))
+    ro, rl = H.oracle_decode(inp, pick)
+    H.assert_close(o[pick], ro, "bf16", "large-batch")
+    H.assert_lse_close(lse[pick], rl, 2e-3, "large-batch")
+
+
+@pytest.mark.parametrize("base,factor", [("c2", -1.0), ("c2", 0.0), ("c5", -1.0)])
+def test_negative_and_zero_scale(base, factor):
+    """The softmax scale enters the formula as given: a negative scale flips
+    the scores (the matrix-core kernel negates the queries, exactly), a zero
+    scale gives the mean latent."""
+    cfg = SMALL[base]
+    scale = factor * cfg.softmax_scale
+    H.say(f"case scale={scale:+.4g} on {base}-reduced")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp, scale=scale)
+    ro, rl = H.oracle_decode(inp, scale=scale)
+    H.assert_close(o, ro, _kind(cfg), f"scale{factor:+g}-{base}")
+    H.assert_lse_close(lse, rl, 2e-3, f"scale{factor:+g}-{base}")
