@@ -132,6 +132,11 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, u
   asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
+// The same copy with a full 64-bit source address per lane.
+__device__ __forceinline__ void lds_dma16_va(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
 __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
@@ -208,6 +213,27 @@ __device__ __forceinline__ void copy_part_f8(int i, const uint8_t* src, const ui
 template <bool B>
 using bool_c = std::integral_constant<bool, B>;
 
+// The lane index, formed afresh where it is used: the empty asm statement
+// keeps the compiler from reusing (and so keeping alive or spilling) an
+// earlier copy. A value reloaded from scratch memory would cost a wait on
+// every vector memory operation in flight, including the cache copies.
+__device__ __forceinline__ uint32_t lane_now() {
+  uint32_t l = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+// floor(g P / G) (the first page of range g), as partition.h defines it, with
+// the quotient estimated in double precision and then corrected to the exact
+// integer (g P stays far below 2^53)
+__device__ __forceinline__ int64_t range_begin_dev(int64_t g, int64_t P, int64_t G) {
+  const int64_t x = g * P;
+  int64_t q = static_cast<int64_t>(static_cast<double>(x) / static_cast<double>(G));
+  while (q > 0 && q * G > x) --q;
+  while ((q + 1) * G <= x) ++q;
+  return q;
+}
+
 // Pointer arguments are separate restrict-qualified parameters, so that the
 // compiler reads the read-only tables with scalar loads.
 //
@@ -227,8 +253,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   constexpr int kS = kFp8 ? kF8Stages : kStages;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kS * kChunkBytes + (kFp8 ? 2 * kF8Stage : 0)];
   __shared__ int restart_flag[4];   // per wave: some row raised its reference in this pass
-  __shared__ int ps_lds[kLdsPlan ? kMaxLdsBatch + 1 : 1];
-  __shared__ int scan_tmp[kLdsPlan ? 256 : 1];
+  __shared__ int ps_lds[kLdsPlan ? kMaxLdsBatch + 1 : 1];   // page prefix sums
+  __shared__ int lens_lds[kLdsPlan ? kMaxLdsBatch : 1];     // clamped sequence lengths
+  __shared__ int wtot_lds[4];                               // per-wave page totals
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -248,31 +275,36 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   if (g >= p.G) return;
   if constexpr (kLdsPlan) {
     // page_start[b] = sum_{b' < b} ceil(S_b' / 64): four sequences per thread,
-    // then a scan over the 256 thread totals
+    // a scan across the wavefront, then the totals of the waves before
     const int t = threadIdx.x;
     int cnt[4], local = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int bb = 4 * t + i;
-      cnt[i] = bb < p.B ? static_cast<int>(pages_of(clamp_len(seq_lens[bb], p.max_blocks))) : 0;
+      const int len = bb < p.B ? clamp_len(seq_lens[bb], p.max_blocks) : 0;
+      if (bb < p.B) lens_lds[bb] = len;
+      cnt[i] = static_cast<int>(pages_of(len));
       local += cnt[i];
     }
-    scan_tmp[t] = local;
-    __syncthreads();
+    int incl = local;
 #pragma unroll
-    for (int off = 1; off < 256; off <<= 1) {
-      const int v = t >= off ? scan_tmp[t - off] : 0;
-      __syncthreads();
-      scan_tmp[t] += v;
-      __syncthreads();
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
     }
-    int run = scan_tmp[t] - local;
+    if (lane == 63) wtot_lds[w] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int ww = 0; ww < w; ++ww) run += wtot_lds[ww];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int bb = 4 * t + i;
       if (bb <= p.B) ps_lds[bb] = run;
       run += cnt[i];
     }
+    // with B = 4 * 256 no thread's sequences reach index B: the last thread
+    // stores the total
+    if (t == 255 && p.B == kMaxLdsBatch) ps_lds[p.B] = run;
     __syncthreads();
     if (blockIdx.x == 0)
       for (int bb = t; bb <= p.B; bb += 256) page_start[bb] = ps_lds[bb];
@@ -282,20 +314,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     else return page_start[i];
   };
   const int64_t P = PS(p.B);
-  const int64_t pb = range_begin(g, P, p.G), pe = range_begin(g + 1, P, p.G);
+  const int64_t pb = range_begin_dev(g, P, p.G), pe = range_begin_dev(g + 1, P, p.G);
   if (pb >= pe) return;
 
+  // first sequence of the range: the number of sequences that end at or
+  // before page pb (the prefix sums are non-decreasing), 64 per ballot
   int b = 0;
-  {
-    int hi = p.B - 1;
-    while (b < hi) {
-      const int mid = (b + hi) >> 1;
-      if (PS(mid + 1) > pb) hi = mid; else b = mid + 1;
-    }
+  for (int j0 = 0; j0 < p.B; j0 += 64) {
+    const int j = j0 + lane;
+    const uint64_t before = __ballot(j < p.B && PS(j + 1) <= pb);
+    b += __popcll(before);
+    if (before != ~0ull) break;
   }
 
-  const int my_row = rg * kMfmaRows + w * 32 + l32;     // the row of this lane's columns
-  const int m = my_row / p.n_h;   // query token of this lane's row
   const float c = p.c_log2;
   const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
@@ -329,7 +360,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     if (s1 == s0) continue;
     const int64_t a0 = s0 > pb ? s0 : pb, a1 = s1 < pe ? s1 : pe;
     const int n_pages = static_cast<int>(a1 - a0);
-    const int S = clamp_len(seq_lens[b], p.max_blocks);
+    int S;
+    if constexpr (kLdsPlan) S = lens_lds[b];
+    else S = clamp_len(seq_lens[b], p.max_blocks);
+    // query token of this lane's row (row / heads), formed per piece from the
+    // lane index
+    const int m = (rg * kMfmaRows + w * 32 + static_cast<int>(lane_now() & 31)) / p.n_h;
     const int pidx0 = static_cast<int>(a0 - s0);
     const int tok0 = pidx0 * 64;
     const int tok1 = min(S, static_cast<int>((a1 - s0) * 64));
@@ -339,20 +375,41 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // row has the smallest query index)
     const int tend_all = min(tok1, S - p.q_len + (rg * kMfmaRows + w * 32) / p.n_h + 1);
     const int32_t* bt = block_table + static_cast<int64_t>(b) * p.max_blocks;
-    // Q^T fragments: per 16-lane k unit, the lane holds lanes [8 half, 8 half + 8)
-    // of its row. The wave's 32 rows are consecutive (row b * rows + my_row),
-    // so the row base is scalar and each lane adds a 32-bit offset.
+    // Q^T fragments: fragment kc of lane (half, l32) holds the 16-byte unit
+    // 2 kc + half of the wave's row l32, where units 0..63 are q_abs and
+    // 64..71 q_rope. The wave's 32 rows are consecutive (rows b * rows +
+    // rg * 128 + 32 w + l32). Loaded straight into that layout, every load
+    // instruction would touch 32 rows; instead each half of the units (36 per
+    // row) is copied HBM -> LDS with whole rows per instruction into a region
+    // of the wave's own, then read in fragment layout. Within a half, row n's
+    // unit v sits at 16-byte slot 36 n + (v ^ ((n >> 2) & 3)): the swizzle
+    // keeps 16 consecutive rows of a fragment read in distinct bank groups.
     bf16x8 qf[36];
-    auto load_q = [&]() {
+    constexpr int kQHalf = 32 * 36 * 16;      // one wave's half: 18 KB
+    auto q_region = [&]() { return lds0 + (kS - 2) * kChunkBytes + w * kQHalf; };
+    auto q_copy = [&](int H) {
       const int64_t qrow0 = static_cast<int64_t>(b) * p.rows + rg * kMfmaRows + w * 32;
-      const uint16_t* qa = q_abs + qrow0 * kDc;
-      const uint16_t* qr = q_rope + qrow0 * kDr;
+      const uint8_t* qa = reinterpret_cast<const uint8_t*>(q_abs + qrow0 * kDc);
+      const uint8_t* qr = reinterpret_cast<const uint8_t*>(q_rope + qrow0 * kDr);
+      const uint32_t li = lane_now();
+      const uint32_t reg = q_region();
 #pragma unroll
-      for (int kc = 0; kc < 32; ++kc)
-        qf[kc] = *reinterpret_cast<const bf16x8*>(qa + l32 * kDc + 16 * kc + 8 * half);
+      for (int i = 0; i < 18; ++i) {
+        const uint32_t sl = 64 * i + li, n = sl / 36, x = sl % 36;
+        const uint32_t u = 36 * H + (x ^ ((n >> 2) & 3));
+        const uint8_t* src = u < 64 ? qa + n * (2 * kDc) + 16 * u : qr + n * (2 * kDr) + 16 * (u - 64);
+        lds_dma16_va(src, reg + 1024 * i);
+      }
+    };
+    auto q_read = [&](int H) {
+      const uint32_t li = lane_now();
+      const uint32_t n = li & 31, hl = li >> 5, sw = (n >> 2) & 3;
+      const uint32_t r0 = q_region() + 576 * n + 16 * (hl ^ sw);          // even fragments
+      const uint32_t r1 = q_region() + 576 * n + 16 * ((2 + hl) ^ sw);    // odd fragments
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qf[32 + kk] = *reinterpret_cast<const bf16x8*>(qr + l32 * kDr + 16 * kk + 8 * half);
+      for (int kc = 0; kc < 18; ++kc)
+        qf[18 * H + kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            static_cast<uintptr_t>(((kc & 1) ? r1 : r0) + 64 * (kc >> 1)));
     };
     auto negate_q = [&]() {   // c s with c < 0 equals |c| (-s), and negating bf16 is exact
 #pragma unroll
@@ -387,19 +444,25 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     auto stage_of = [&](int q) { return lds0 + static_cast<uint32_t>(q % kS) * kChunkBytes; };
     const uint32_t stg0 = lds0 + kS * kChunkBytes;   // fp8 staging buffers
     // copy all of chunk q at once (into its stage, or for fp8 its staging buffer)
+    // (the per-lane offsets are formed afresh: see lane_now)
     auto issue = [&](int q) {
       const uint8_t* src = chunk_src(q);
       const int nv = chunk_valid(q);
+      const int li = static_cast<int>(lane_now());
       if constexpr (kFp8) {
         const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
             cache_scale + chunk_page(q) * 64 + (q & 1) * kChunk);
 #pragma unroll
         for (int i = 0; i < kF8CopiesPerChunk; ++i)
-          copy_part_f8(i, src, ssrc, nv, stg0 + (q & 1) * kF8Stage, w, lane);
+          copy_part_f8(i, src, ssrc, nv, stg0 + (q & 1) * kF8Stage, w, li);
       } else {
+        CopyPlan cpi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cpi.content[i] = (li ^ swz(4 * w + i)) << 4;
+        cpi.rope = rope_src(w, li, kChunk);
 #pragma unroll
         for (int i = 0; i < kCopiesPerChunk; ++i)
-          copy_part(i, src, nv, stage_of(q), w, lane, cp);
+          copy_part(i, src, nv, stage_of(q), w, li, cpi);
       }
     };
     // fp8: dequantise chunk q from its staging buffer into its bf16 stage:
@@ -409,7 +472,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // scale 0. Every wave must have waited for the copies (and passed a
     // barrier) before, and a barrier must follow before the stage is read.
     auto dequant = [&](int q) {
-      const int t = threadIdx.x >> 3, gq = threadIdx.x & 7;
+      const int tid = w * 64 + static_cast<int>(lane_now());
+      const int t = tid >> 3, gq = tid & 7;
       const uint32_t sb = stg0 + (q & 1) * kF8Stage;
       const uint32_t db = stage_of(q);
       const float sc = t < chunk_valid(q)
@@ -662,28 +726,31 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     zero_o();
     clear_prev();
     __syncthreads();   // earlier reads of every stage are done
-    if constexpr (kFp8) {
-      // chunks 0 and 1, then the queries: chunk 0 is dequantised while the
-      // queries are still in flight
-      issue(0);
-      if (n > 1) issue(1);
-      load_q();
-      if (n > 1) MLA_WAIT_VM(kF8CopiesPerChunk + 36);
-      else MLA_WAIT_VM(36);
-      __syncthreads();
-      dequant(0);
-      MLA_WAIT_VM(0);
+    // nothing of this piece is in flight yet: a full wait here also completes
+    // any reload of a spilled value the compiler placed before this point,
+    // so that no wait for it lands among the copies below
+    MLA_WAIT_VM(0);
+    // Prologue: the first half of the queries and chunk 0 in flight; the
+    // half read into registers; the second half and chunk 1 in flight; wait
+    // for all but chunk 1 (copies complete in order). The query regions are
+    // the ring's last two stages, which chunks 0 and 1 do not use.
+    constexpr int kCopies = kFp8 ? kF8CopiesPerChunk : kCopiesPerChunk;
+    q_copy(0);
+    issue(0);
+    MLA_WAIT_VM(kCopies);          // this wave's first query half
+    q_read(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before it is overwritten
+    q_copy(1);
+    if (n > 1) {
+      issue(1);
+      MLA_WAIT_VM(kCopies);        // the second half and chunk 0
     } else {
-      // chunk 0, the queries, chunk 1: waiting for all but chunk 1's copies
-      // then covers the queries too
-      issue(0);
-      load_q();
-      if (n > 1) {
-        issue(1);
-        MLA_WAIT_VM(kCopiesPerChunk);
-      } else {
-        MLA_WAIT_VM(0);
-      }
+      MLA_WAIT_VM(0);
+    }
+    q_read(1);
+    if constexpr (kFp8) {
+      __syncthreads();             // every wave's copies of chunk 0 have landed
+      dequant(0);
     }
     if (p.neg_q) negate_q();
     // Chunk loop. A row whose max rose past the lazy threshold makes its wave
@@ -785,7 +852,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       }
     }
     if (half == 0)
-      lse_part[slot * p.rows + my_row] =
+      lse_part[slot * p.rows + rg * kMfmaRows + w * 32 + static_cast<int>(lane_now() & 31)] =
           l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
   }
 }

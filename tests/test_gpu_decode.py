@@ -206,6 +206,21 @@ def test_batch_above_the_in_kernel_prefix_limit():
     H.assert_lse_close(lse[pick], rl, 2e-3, "large-batch")
 
 
+@pytest.mark.parametrize("batch", [1023, 1024])
+def test_batch_at_the_in_kernel_prefix_limit(batch):
+    """1023 and 1024 sequences: the largest batches whose page prefix sums
+    the matrix-core kernel forms itself (at 1024 no thread's sequences reach
+    index B, so the total is stored separately)."""
+    cfg = wl.scaled(C["c4"], batch=batch, ragged=(1, 130))
+    H.say(f"case batch B={cfg.batch} lens={cfg.ragged} (in-kernel prefix sums)")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    pick = sorted({0, 1, 2, 255, 256, 511, 767, 1020, batch - 2, batch - 1} | set(range(100, batch, 89)))
+    ro, rl = H.oracle_decode(inp, pick)
+    H.assert_close(o[pick], ro, "bf16", f"batch{batch}")
+    H.assert_lse_close(lse[pick], rl, 2e-3, f"batch{batch}")
+
+
 @pytest.mark.parametrize("base,factor", [("c2", -1.0), ("c2", 0.0), ("c5", -1.0)])
 def test_negative_and_zero_scale(base, factor):
     """The softmax scale enters the formula as given: a negative scale flips
