@@ -131,9 +131,10 @@ mla_status mla_decode(const mla_decode_desc* d, const void* q_abs, const void* q
  * token range of the same sequences).
  *
  * mla_decode_partial: the plan (unless plan_ready) and the split-KV kernel
- * only. It leaves, in the workspace, the softmax-normalised partial output
- * and log-sum-exp of every (page range, sequence) piece; arguments as in
- * mla_decode.
+ * only. It leaves, in the workspace, the partial output and log-sum-exp of
+ * every (page range, sequence) piece (the matrix-core kernel leaves the
+ * partial unnormalised, with its softmax row sum beside it); arguments as in
+ * mla_decode. The workspace layout is private to the library.
  * mla_decode_combine: the log-sum-exp merge of those partials into
  * o_latent / lse_out (LSE = ln sum_r exp(lse_r), o = sum_r exp(lse_r - LSE) o_r),
  * exactly the softmax over all tokens ([Zhang] "Value absorption": one

@@ -74,7 +74,8 @@ mla_status make_plan(const mla_decode_desc* d, DecodePlan* p) {
   p->plan_off = 0;
   p->opart_off = align256(sizeof(int32_t) * (static_cast<size_t>(d->batch) + 1));
   p->lse_off = align256(p->opart_off + sizeof(float) * static_cast<size_t>(p->slots) * rows * d->d_c);
-  p->total = align256(p->lse_off + sizeof(float) * static_cast<size_t>(p->slots) * rows);
+  p->lsum_off = align256(p->lse_off + sizeof(float) * static_cast<size_t>(p->slots) * rows);
+  p->total = align256(p->lsum_off + sizeof(float) * static_cast<size_t>(p->slots) * rows);
   return MLA_OK;
 }
 
@@ -145,6 +146,7 @@ mla_status prepare(const mla_decode_desc* d, const void* q_abs, const void* q_ro
   a->scale = scale;
   a->o_part = ws + p->opart_off;
   a->lse_part = reinterpret_cast<float*>(ws + p->lse_off);
+  a->l_part = p->path == Path::Mfma ? reinterpret_cast<float*>(ws + p->lsum_off) : nullptr;
   a->o_latent = nullptr;
   a->lse_out = nullptr;
   return MLA_OK;
@@ -215,6 +217,7 @@ mla_status mla_decode_combine(const mla_decode_desc* d, void* workspace, size_t 
   a.page_start = reinterpret_cast<const int32_t*>(ws + p.plan_off);
   a.o_part = ws + p.opart_off;
   a.lse_part = reinterpret_cast<float*>(ws + p.lse_off);
+  a.l_part = p.path == Path::Mfma ? reinterpret_cast<float*>(ws + p.lsum_off) : nullptr;
   a.o_latent = o_latent;
   a.lse_out = lse_out;
   return launch_combine(a, static_cast<hipStream_t>(stream));

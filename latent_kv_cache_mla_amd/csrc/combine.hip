@@ -57,7 +57,9 @@ __device__ __forceinline__ void load8(const uint16_t* p, float* v) {
 
 // kWR wavefronts per output row (sequence b, row r); with kWR = 1 a block
 // holds four rows. Lane j of every wavefront loads the log-sum-exp of range j
-// of the row's ranges (64 at a time) and forms its weight exp(lse_j - LSE);
+// of the row's ranges (64 at a time) and forms its weight exp(lse_j - LSE),
+// divided by the partial's softmax row sum where the partials are
+// unnormalised (l_part non-null);
 // wavefront q then combines 8 consecutive latent lanes per lane over ranges
 // q, q + kWR, ..., with eight partial loads in flight, and the kWR partial
 // sums are added through LDS. Several wavefronts per row serve sequences cut
@@ -66,6 +68,7 @@ template <typename PT, int OT, int kWR>  // partial element type, output dtype, 
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
+                                                      const float* __restrict__ l_part,
                                                       void* __restrict__ o_latent,
                                                       float* __restrict__ lse_out,
                                                       int B, int rows, int d_c, int64_t G) {
@@ -95,6 +98,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     if (may_be_empty && range_begin(g + 1, P, G) == range_begin(g, P, G)) return -INFINITY;
     return lse_part[slot_of(g, b) * rows + r];
   };
+  // 1 / row sum of range j's partial when the partials are unnormalised
+  auto rl_of = [&](int64_t j) {
+    return l_part != nullptr ? 1.f / l_part[slot_of(glo + j, b) * rows + r] : 1.f;
+  };
   // lane j holds the log-sum-exp of range j (up to 64 ranges in registers;
   // rows with more ranges reload them per block of 64)
   float l0 = n > 0 && lane < n ? lse_of(lane) : -INFINITY;
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     for (int64_t j0 = 0; j0 < n && mx != -INFINITY; j0 += 64) {
       float lj = l0;
       if (j0 > 0) lj = j0 + lane < n ? lse_of(j0 + lane) : -INFINITY;
-      const float wj = lj == -INFINITY ? 0.f : expf(lj - mx) * inv;
+      const float wj = lj == -INFINITY ? 0.f : expf(lj - mx) * inv * rl_of(j0 + lane);
       const int cnt = static_cast<int>(n - j0 < 64 ? n - j0 : 64);
       for (int j = q; j < cnt; j += 8 * kWR) {
         float wgt[8], v[8][8];
@@ -186,13 +193,13 @@ void launch_combine_t(const DecodeArgs& a, const PT* op, hipStream_t st) {
   const dim3 block(256), grid(static_cast<unsigned>((pairs * wr + 3) / 4));
   if (wr == 4)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 4>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
   else if (wr == 2)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 2>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
   else
     hipLaunchKernelGGL((combine_kernel<PT, OT, 1>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
 }
 
 mla_status launch_combine(const DecodeArgs& a, hipStream_t st) {

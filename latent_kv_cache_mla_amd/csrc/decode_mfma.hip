@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint8_t* __restrict__ cache, const float* __restrict__ cache_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     int32_t* __restrict__ page_start, void* __restrict__ o_part, float* __restrict__ lse_part,
-    MfmaParams p) {
+    float* __restrict__ l_part, MfmaParams p) {
   // ring of bf16 chunk stages: chunk k lives in stage k % kS (fp8: plus two
   // staging buffers after the ring)
   constexpr int kS = kFp8 ? kF8Stages : kStages;
@@ -436,12 +436,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     };
     // first cached row of chunk q of the piece (the page id is a scalar load)
     constexpr int kRow = kFp8 ? kF8Row : kRowBytes;
-    auto chunk_page = [&](int q) -> int64_t { return bt[pidx0 + (q >> 1)]; };
+    auto chunk_page = [&](int q) -> int { return bt[pidx0 + (q >> 1)]; };
     auto chunk_src = [&](int q) {
       return cache + chunk_page(q) * (64LL * kRow) + (q & 1) * (kChunk * kRow);
     };
     auto chunk_valid = [&](int q) { return min(kChunk, tok1 - tok0 - kChunk * q); };
-    auto stage_of = [&](int q) { return lds0 + static_cast<uint32_t>(q % kS) * kChunkBytes; };
+    auto stage_of = [&](int q) { return lds0 + (static_cast<uint32_t>(q) % kS) * kChunkBytes; };
     const uint32_t stg0 = lds0 + kS * kChunkBytes;   // fp8 staging buffers
     // copy all of chunk q at once (into its stage, or for fp8 its staging buffer)
     // (the per-lane offsets are formed afresh: see lane_now)
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       const int li = static_cast<int>(lane_now());
       if constexpr (kFp8) {
         const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
-            cache_scale + chunk_page(q) * 64 + (q & 1) * kChunk);
+            cache_scale + static_cast<int64_t>(chunk_page(q)) * 64 + (q & 1) * kChunk);
 #pragma unroll
         for (int i = 0; i < kF8CopiesPerChunk; ++i)
           copy_part_f8(i, src, ssrc, nv, stg0 + (q & 1) * kF8Stage, w, li);
@@ -588,20 +588,45 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // keeps O in the accumulation registers: step 0 weighs chunk 0 with the
     // zero probabilities of the empty chunk -1, and step n multiplies a stage
     // whose scores the mask removes entirely.
-    auto step = [&](int k) {
+    // pg: page id of chunk k + 2, which the step copies. Its scalar load is
+    // issued before the barrier that opens the step and used at the top of
+    // the step, before any LDS read: a scalar load still in flight makes the
+    // compiler wait for every LDS read in flight at its next LDS wait.
+    auto step = [&](int k, int pg) {
       const uint32_t bq = stage_of(k);
       const uint32_t bv = k == 0 ? bq : stage_of(k + kS - 1);
       // stage (k + 2) % 4 last held chunk k - 2, whose weighted sum every
       // wave finished before the barrier that opened this step (the fp8 path
       // copies outside the step)
       const bool copy = k + 2 < n;
-      const uint8_t* csrc = copy ? chunk_src(k + 2) : cache;
       const int cnv = copy ? chunk_valid(k + 2) : kChunk;
+      // the copy sources of chunk k + 2, formed here at the top of the step,
+      // where no LDS read is in flight
+      const int64_t pgc = pg;
+      const uint8_t* csrc = cache + pgc * (64LL * kRow) + ((k + 2) & 1) * (kChunk * kRow);
+      const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
+          cache_scale + pgc * 64 + ((k + 2) & 1) * kChunk);
+      asm volatile("" : "+s"(csrc));
+      if constexpr (kFp8) asm volatile("" : "+s"(ssrc));
       const uint32_t cbuf = stage_of(k + 2);
-      // fp8: the scale rows of chunk k + 2, and whether chunk k + 1 is to be
-      // dequantised in this step
-      const uint8_t* ssrc = kFp8 && copy ? reinterpret_cast<const uint8_t*>(
-          cache_scale + chunk_page(k + 2) * 64 + ((k + 2) & 1) * kChunk) : cache;
+      // full chunks are copied in nine pieces spread over the score MFMAs
+      // (rows 4 w + j and 16 + 4 w + j, then the rope rows); a partial last
+      // chunk is copied at once
+      const bool cfast = copy && cnv == kChunk;
+      const uint8_t* csw = csrc + 4 * w * kRowBytes;
+      const uint32_t cbw = cbuf + 4 * w * 1024;
+      auto copy_fast = [&](int i) {
+        if (i < 8) {
+          const int t = 16 * (i >> 2) + (i & 3);
+          lds_dma16(csw + t * kRowBytes, cp.content[i & 3], cbw + t * 1024);
+        } else {
+          lds_dma16(csrc, cp.rope, cbuf + kChunkContent + w * 1024);
+        }
+      };
+      if constexpr (!kFp8) {
+        if (copy && !cfast) issue(k + 2);
+      }
+      // fp8: whether chunk k + 1 is to be dequantised in this step
       const bool dq = kFp8 && k + 1 < n;
       // the fragment bases pass through an empty asm statement, so that the
       // per-fragment XOR variants are formed here, step by step, instead of
@@ -669,7 +694,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           if ((kc & 3) == 2 && kc < 24 && copy)
             copy_part_f8(kc >> 2, csrc, ssrc, cnv, stg0 + ((k + 2) & 1) * kF8Stage, w, tid_s & 63);
         } else {
-          if ((kc & 3) == 2 && copy) copy_part(kc >> 2, csrc, cnv, cbuf, w, lane, cp);
+          if ((kc & 3) == 2 && cfast) copy_fast(kc >> 2);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -758,6 +783,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // from its first chunk with the raised maxima (every wave sees the same
     // flags, so all restart together).
     for (int k = 0; k <= n; ++k) {
+      const int pg = k + 2 < n ? chunk_page(k + 2) : 0;
       if constexpr (kFp8) {
         // chunk k was dequantised in the previous step (or the prologue);
         // chunk k + 1 must have landed in its staging buffer
@@ -773,7 +799,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         }
         __syncthreads();     // ... and every other wave's
       }
-      step(k);
+      step(k, pg);
       if (k == n) {        // end of the pass: no copy is in flight
         const bool any_raise = __any(raise);
         if (lane == 0) restart_flag[w] = any_raise ? 1 : 0;
@@ -789,71 +815,71 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       }
     }
 
-    // ---- epilogue: normalised partial and its log-sum-exp ----
-    // O^T sits in the MFMA layout (lane = row, registers = columns); the rows
-    // go through LDS so that each store instruction writes 1 KB of one row.
-    // LDS rows are padded to 1040 bytes, which spreads the 32 rows a write
-    // instruction touches over the banks, while every offset stays a
-    // compile-time immediate on one per-lane base.
+    // ---- epilogue: the unnormalised partial, its row sum and log-sum-exp ----
+    // O^T sits in the MFMA layout (lane = row, registers = columns). Four
+    // passes of 128 columns each: the wave stores its 32 x 128 fp32 block
+    // into LDS straight from the accumulation registers (no vector-ALU work),
+    // then reads it back two rows per instruction and writes coalesced rows.
+    // The combine divides by the row sum (l_part), which saves the 256
+    // per-lane multiplications a normalisation here would cost.
+    // LDS rows are 528 bytes (128 fp32 + 16): the 16 rows of a write
+    // instruction's lane group then fall in distinct bank groups.
     const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     const int64_t slot = slot_of(g, b);
-    constexpr int kEpiRow = 1040;
-    const uint32_t lrow = lds0 + (w * 32 + l32) * kEpiRow + 8 * half;
-    const uint32_t lrd = lds0 + w * 32 * kEpiRow + 16 * lane;
+    constexpr int kEpiRow = 528;
+    const uint32_t li = lane_now();
+    const uint32_t ewave = lds0 + w * 32 * kEpiRow;
+    const uint32_t ewr = ewave + (li & 31) * kEpiRow + (li >> 5) * 16;   // row l32, unit half
+    const uint32_t erd = ewave + (li >> 5) * kEpiRow + (li & 31) * 16;   // row li / 32, unit li % 32
+    const int64_t row0 = slot * p.rows + rg * kMfmaRows + w * 32;
     __syncthreads();                           // every wave is done with the stages
-    if (p.part_bf16) {
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb)
+    for (int qq = 0; qq < 4; ++qq) {
+      // columns 32 mb + 8 j + 4 half + (0..3) of tile mb = 4 qq + t sit in
+      // registers 4 j .. 4 j + 3: LDS bytes 128 t + 32 j of the row's unit half
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // columns 32 mb + 8 j + 4 half + (0..3): 16-byte unit 4 mb + j, bytes 8 half
-          const bf16x2 lo = {static_cast<__bf16>(o[mb][4 * j] * inv), static_cast<__bf16>(o[mb][4 * j + 1] * inv)};
-          const bf16x2 hi = {static_cast<__bf16>(o[mb][4 * j + 2] * inv), static_cast<__bf16>(o[mb][4 * j + 3] * inv)};
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          const u32x2 v = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-              static_cast<uintptr_t>(lrow + (4 * mb + j) * 16)) = v;
-        }
-      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's rows are in LDS
+      for (int t = 0; t < 4; ++t) {
+        const f32x16& ot = o[4 * qq + t];
+        const f32x4 q0 = ot.s0123, q1 = ot.s4567, q2 = ot.s89ab, q3 = ot.scdef;
+        asm volatile("ds_write_b128 %0, %1 offset:%2" :: "v"(ewr), "a"(q0), "i"(128 * t) : "memory");
+        asm volatile("ds_write_b128 %0, %1 offset:%2" :: "v"(ewr), "a"(q1), "i"(128 * t + 32) : "memory");
+        asm volatile("ds_write_b128 %0, %1 offset:%2" :: "v"(ewr), "a"(q2), "i"(128 * t + 64) : "memory");
+        asm volatile("ds_write_b128 %0, %1 offset:%2" :: "v"(ewr), "a"(q3), "i"(128 * t + 96) : "memory");
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the block is in LDS
       __builtin_amdgcn_wave_barrier();
-      uint16_t* dst = static_cast<uint16_t*>(o_part) +
-                      (slot * p.rows + rg * kMfmaRows + w * 32) * static_cast<int64_t>(kDc) + 8 * lane;
-#pragma unroll 8
-      for (int rr = 0; rr < 32; ++rr) {
-        const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            static_cast<uintptr_t>(lrd + rr * kEpiRow));
-        *reinterpret_cast<f32x4*>(dst + rr * kDc) = v;
-      }
-    } else {
-      float* dst = static_cast<float*>(o_part) +
-                   (slot * p.rows + rg * kMfmaRows + w * 32) * static_cast<int64_t>(kDc) + 4 * lane;
+      // rows 2 s2 and 2 s2 + 1 per instruction: a scalar row base plus the
+      // lane's offset (row li / 32, columns 128 qq + 4 (li % 32) ...)
+      // (all 16 reads of the pass are issued before the first conversion)
+      const uint32_t eoff = (li >> 5) * kDc + 4 * (li & 31);
+      f32x4 ev[16];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {         // columns [256 hh, 256 hh + 256): 1 KB per row
+      for (int s2 = 0; s2 < 16; ++s2)
+        ev[s2] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            static_cast<uintptr_t>(erd + 2 * s2 * kEpiRow));
+      if (p.part_bf16) {
+        uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + 128 * qq;
 #pragma unroll
-        for (int mb = 8 * hh; mb < 8 * hh + 8; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            // columns 32 mb + 8 j + 4 half + (0..3) - 256 hh: unit 2 (4 (mb - 8 hh) + j) + half
-            const f32x4 v = f32x4{o[mb][4 * j], o[mb][4 * j + 1], o[mb][4 * j + 2], o[mb][4 * j + 3]} * inv;
-            *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(
-                lrow + 8 * half + (2 * (4 * (mb - 8 * hh) + j)) * 16)) = v;
-          }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll 8
-        for (int rr = 0; rr < 32; ++rr) {
-          const f32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-              static_cast<uintptr_t>(lrd + rr * kEpiRow));
-          *reinterpret_cast<f32x4*>(dst + rr * kDc + 256 * hh) = v;
+        for (int s2 = 0; s2 < 16; ++s2) {
+          const bf16x2 lo = {static_cast<__bf16>(ev[s2][0]), static_cast<__bf16>(ev[s2][1])};
+          const bf16x2 hi = {static_cast<__bf16>(ev[s2][2]), static_cast<__bf16>(ev[s2][3])};
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const u32x2 u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          *reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff) = u;
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
+      } else {
+        float* ob = static_cast<float*>(o_part) + row0 * kDc + 128 * qq;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) *reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff) = ev[s2];
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // the reads are done before the next pass
+      __builtin_amdgcn_wave_barrier();
     }
-    if (half == 0)
-      lse_part[slot * p.rows + rg * kMfmaRows + w * 32 + static_cast<int>(lane_now() & 31)] =
-          l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+    if ((li >> 5) == 0) {
+      const int64_t r = slot * p.rows + rg * kMfmaRows + w * 32 + static_cast<int>(li & 31);
+      lse_part[r] = l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+      l_part[r] = l_row;
+    }
   }
 }
 
@@ -891,7 +917,7 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
                      a.cache_scale, a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start),
-                     a.o_part, a.lse_part, p);
+                     a.o_part, a.lse_part, a.l_part, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
   return MLA_OK;

@@ -26,7 +26,7 @@ struct DecodePlan {
   int64_t G;         // number of page ranges (partitions)
   int64_t slots;     // G + B partial slots
   int part_bf16;     // partials stored as bf16 (MFMA path with a bf16 output), else fp32
-  size_t plan_off, opart_off, lse_off, total;  // workspace layout (bytes)
+  size_t plan_off, opart_off, lse_off, lsum_off, total;  // workspace layout (bytes)
 };
 
 // Validates the descriptor (sets the thread's last error) and lays out the
@@ -54,6 +54,9 @@ struct DecodeArgs {
   float scale;
   void* o_part;      // bf16 or fp32, per DecodePlan::part_bf16
   float* lse_part;
+  // row sums of unnormalised partials (MFMA path); nullptr: the partials are
+  // already normalised (generic path)
+  float* l_part;
   void* o_latent;
   float* lse_out;
 };
