@@ -40,30 +40,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (t == 1023) page_start[B] = part[1023];
 }
 
-// 8 consecutive partial elements of one row, as fp32
-__device__ __forceinline__ void load8(const float* p, float* v) {
-  const float4 x = *reinterpret_cast<const float4*>(p), y = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
-}
-__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
-  const uint4 x = *reinterpret_cast<const uint4*>(p);
-  const uint32_t u[4] = {x.x, x.y, x.z, x.w};
+// Raw 8-element partial loads (bf16 or fp32) and their conversion to fp32:
+// the loads of a batch are all issued before any value is used.
+template <typename PT> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 x;
+  __device__ __forceinline__ void load(const uint16_t* p) { x = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { x = make_uint4(0u, 0u, 0u, 0u); }
+  __device__ __forceinline__ void get(float* v) const {
+    const uint32_t u[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(u[i] << 16);
-    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
   }
-}
+};
+template <> struct Raw8<float> {
+  float4 x, y;
+  __device__ __forceinline__ void load(const float* p) {
+    x = *reinterpret_cast<const float4*>(p);
+    y = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { x = y = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void get(float* v) const {
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  }
+};
 
-// kWR wavefronts per output row (sequence b, row r); with kWR = 1 a block
-// holds four rows. Lane j of every wavefront loads the log-sum-exp of range j
-// of the row's ranges (64 at a time) and forms its weight exp(lse_j - LSE),
-// divided by the partial's softmax row sum where the partials are
-// unnormalised (l_part non-null);
-// wavefront q then combines 8 consecutive latent lanes per lane over ranges
-// q, q + kWR, ..., with eight partial loads in flight, and the kWR partial
-// sums are added through LDS. Several wavefronts per row serve sequences cut
-// into many ranges (long contexts with a small batch).
+// kWR wavefronts per output row (sequence b, row r); a block holds 4 / kWR
+// rows. The row's ranges [glo, glo + n) follow from the page prefix sums by
+// the partition arithmetic. Wavefront q takes ranges q, q + kWR, ...: it
+// forms the max m_q and sum s_q of exp(lse_j - m_q) over them and the sum of
+// exp(lse_j - m_q) o_j (o_j divided by its row sum where the partials are
+// unnormalised); lane l holds latent lanes [8 l, 8 l + 8). The log-sum-exps
+// are uniform per row and read with scalar loads, so no lane exchange is
+// needed; the first eight partial loads are issued before them. The
+// wavefronts of a row then merge through LDS: M = max m_q,
+// S = sum s_q exp(m_q - M), o = sum_q acc_q exp(m_q - M) / S.
 template <typename PT, int OT, int kWR>  // partial element type, output dtype, waves per row
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
@@ -74,10 +88,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       int B, int rows, int d_c, int64_t G) {
   static_assert(kWR == 1 || kWR == 2 || kWR == 4, "waves per row");
   __shared__ float red[kWR > 1 ? 4 : 1][kWR > 1 ? 64 * 8 : 1];   // per wavefront of the block
+  __shared__ float wms[4][2];                                     // (m_q, s_q) per wavefront
   const int lane = threadIdx.x & 63;
-  const int wv = static_cast<int>(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int q = wv % kWR;
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (4 / kWR) + (threadIdx.x >> 6) / kWR;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (4 / kWR) + wv / kWR;
   if (pair >= static_cast<int64_t>(B) * rows) return;   // uniform per row's wavefronts
   const int64_t b = pair / rows;
   const int r = static_cast<int>(pair % rows);
@@ -89,88 +104,122 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   // pages some ranges are empty and wrote nothing (weight 0, never read)
   int64_t glo = 0, n = 0;
   if (s1 > s0) {
-    glo = range_of_page(s0, P, G);
-    n = range_of_page(s1 - 1, P, G) - glo + 1;
+    glo = range_of_page_dev(s0, P, G);
+    n = range_of_page_dev(s1 - 1, P, G) - glo + 1;
   }
   const bool may_be_empty = G > P;
-  auto lse_of = [&](int64_t j) {
-    const int64_t g = glo + j;
-    if (may_be_empty && range_begin(g + 1, P, G) == range_begin(g, P, G)) return -INFINITY;
-    return lse_part[slot_of(g, b) * rows + r];
+  auto nonempty = [&](int64_t j) {
+    return !may_be_empty || range_begin_dev(glo + j + 1, P, G) != range_begin_dev(glo + j, P, G);
   };
-  // 1 / row sum of range j's partial when the partials are unnormalised
-  auto rl_of = [&](int64_t j) {
-    return l_part != nullptr ? 1.f / l_part[slot_of(glo + j, b) * rows + r] : 1.f;
-  };
-  // lane j holds the log-sum-exp of range j (up to 64 ranges in registers;
-  // rows with more ranges reload them per block of 64)
-  float l0 = n > 0 && lane < n ? lse_of(lane) : -INFINITY;
-  float mx = l0;
-  for (int64_t j = lane + 64; j < n; j += 64) mx = fmaxf(mx, lse_of(j));
-  mx = wave_max(mx);
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    wsum = l0 == -INFINITY ? 0.f : expf(l0 - mx);
-    for (int64_t j = lane + 64; j < n; j += 64) {
-      const float l = lse_of(j);
-      if (l != -INFINITY) wsum += expf(l - mx);
+  auto idx = [&](int64_t j) { return slot_of(glo + j, b) * rows + r; };
+  auto lse_of = [&](int64_t j) { return nonempty(j) ? lse_part[idx(j)] : -INFINITY; };
+
+  // the first batch of this wavefront's partials (column block 0)
+  Raw8<PT> raw[8];
+  {
+    const int c0 = 8 * lane;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = q + u * kWR;
+      if (j < n && c0 < d_c && nonempty(j)) raw[u].load(o_part + idx(j) * d_c + c0);
+      else raw[u].zero();
     }
   }
-  wsum = wave_sum(wsum);
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  // The log-sum-exps and row sums are uniform per row: scalar loads, eight
+  // ranges at a time, all issued before any is used.
+  float mq = -INFINITY;   // max of this wavefront's log-sum-exps
+  for (int64_t j0 = q; j0 < n; j0 += 8 * kWR) {
+    float lb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + u * kWR;
+      lb[u] = j < n ? lse_part[idx(j)] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = j0 + u * kWR;
+      if (j < n && nonempty(j)) mq = fmaxf(mq, lb[u]);
+    }
+  }
+  float sq = 0.f;   // sum of exp(lse_j - m_q) over this wavefront's ranges
 
   // the column loop is uniform across the block (barriers inside)
   for (int cb = 0; cb < d_c; cb += 512) {
     const int c0 = cb + 8 * lane;
     const bool act = c0 < d_c;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int64_t j0 = 0; j0 < n && mx != -INFINITY; j0 += 64) {
-      float lj = l0;
-      if (j0 > 0) lj = j0 + lane < n ? lse_of(j0 + lane) : -INFINITY;
-      const float wj = lj == -INFINITY ? 0.f : expf(lj - mx) * inv * rl_of(j0 + lane);
-      const int cnt = static_cast<int>(n - j0 < 64 ? n - j0 : 64);
-      for (int j = q; j < cnt; j += 8 * kWR) {
-        float wgt[8], v[8][8];
+    for (int64_t j0 = q; j0 < n && mq != -INFINITY; j0 += 8 * kWR) {
+      if (cb > 0 || j0 > q) {   // later batches: load now
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int jj = j + u * kWR;
-          wgt[u] = jj < cnt ? __shfl(wj, jj, 64) : 0.f;   // uniform
-          if (wgt[u] != 0.f && act)
-            load8(o_part + (slot_of(glo + j0 + jj, b) * rows + r) * static_cast<int64_t>(d_c) + c0, v[u]);
+          const int64_t j = j0 + u * kWR;
+          if (j < n && act && nonempty(j)) raw[u].load(o_part + idx(j) * d_c + c0);
+          else raw[u].zero();
         }
+      }
+      float lb[8], rb[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (wgt[u] != 0.f && act)
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + u * kWR;
+        lb[u] = j < n ? lse_part[idx(j)] : -INFINITY;
+        rb[u] = j < n && l_part != nullptr ? l_part[idx(j)] : 1.f;
+      }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wgt[u], v[u][i], acc[i]);
+      for (int u = 0; u < 8; ++u) {
+        const int64_t j = j0 + u * kWR;
+        if (j >= n) break;
+        if (!nonempty(j) || lb[u] == -INFINITY) continue;
+        const float e = expf(lb[u] - mq);
+        if (cb == 0) sq += e;
+        const float w = e / rb[u];
+        float v[8];
+        raw[u].get(v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
       }
     }
+    // merge the row's wavefronts: M, S and the rescaled sums
+    float M = mq, S = sq;
     if constexpr (kWR > 1) {
       __syncthreads();   // an earlier column block's sums have been read
 #pragma unroll
       for (int i = 0; i < 8; ++i) red[wv][lane * 8 + i] = acc[i];
+      if (lane == 0) { wms[wv][0] = mq; wms[wv][1] = sq; }
       __syncthreads();
       if (q != 0) continue;
+      M = -INFINITY;
+      for (int qq = 0; qq < kWR; ++qq) M = fmaxf(M, wms[wv + qq][0]);
+      if (M != -INFINITY) {
+        S = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        for (int qq = 1; qq < kWR; ++qq) acc[i] += red[wv + qq][lane * 8 + i];
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int qq = 0; qq < kWR; ++qq) {
+          const float mo = wms[wv + qq][0];
+          if (mo == -INFINITY) continue;
+          const float f = expf(mo - M);
+          S += wms[wv + qq][1] * f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(f, red[wv + qq][lane * 8 + i], acc[i]);
+        }
+      }
     }
+    const float inv = S > 0.f ? 1.f / S : 0.f;
+    if (cb == 0 && lse_out != nullptr && lane == 0)
+      lse_out[pair] = S > 0.f ? M + logf(S) : -INFINITY;
     if (!act) continue;
     if constexpr (OT == MLA_FP32) {
       float* o = static_cast<float*>(o_latent) + out_row + c0;
-      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
     } else {
       uint32_t u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        u[i] = f32_to_bf16(acc[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+        u[i] = f32_to_bf16(acc[2 * i] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] * inv)) << 16);
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(o_latent) + out_row + c0) =
           make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
-  if (lse_out != nullptr && lane == 0 && q == 0)
-    lse_out[pair] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
 }  // namespace

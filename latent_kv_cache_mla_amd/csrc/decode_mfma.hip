@@ -223,16 +223,6 @@ __device__ __forceinline__ uint32_t lane_now() {
   return l;
 }
 
-// floor(g P / G) (the first page of range g), as partition.h defines it, with
-// the quotient estimated in double precision and then corrected to the exact
-// integer (g P stays far below 2^53)
-__device__ __forceinline__ int64_t range_begin_dev(int64_t g, int64_t P, int64_t G) {
-  const int64_t x = g * P;
-  int64_t q = static_cast<int64_t>(static_cast<double>(x) / static_cast<double>(G));
-  while (q > 0 && q * G > x) --q;
-  while ((q + 1) * G <= x) ++q;
-  return q;
-}
 
 // Pointer arguments are separate restrict-qualified parameters, so that the
 // compiler reads the read-only tables with scalar loads.

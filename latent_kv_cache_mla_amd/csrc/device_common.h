@@ -26,6 +26,25 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
+// floor(a / d) for 0 <= a, 0 < d: a double-precision estimate corrected to
+// the exact integer (the integer division it replaces is a long instruction
+// sequence on this hardware)
+__device__ __forceinline__ int64_t floordiv_dev(int64_t a, int64_t d) {
+  int64_t q = static_cast<int64_t>(static_cast<double>(a) / static_cast<double>(d));
+  while (q > 0 && q * d > a) --q;
+  while ((q + 1) * d <= a) ++q;
+  return q;
+}
+
+// range_begin and range_of_page of partition.h, with floordiv_dev
+__device__ __forceinline__ int64_t range_begin_dev(int64_t g, int64_t P, int64_t G) {
+  return floordiv_dev(g * P, G);
+}
+__device__ __forceinline__ int64_t range_of_page_dev(int64_t x, int64_t P, int64_t G) {
+  const int64_t g = floordiv_dev((x + 1) * G + P - 1, P) - 1;
+  return g < G - 1 ? g : G - 1;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
