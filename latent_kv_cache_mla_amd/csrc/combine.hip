@@ -126,20 +126,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     }
   }
   // The log-sum-exps and row sums are uniform per row: scalar loads, eight
-  // ranges at a time, all issued before any is used.
+  // ranges at a time, all issued before any is used. The first batch's are
+  // kept for its weights; a row with more ranges per wavefront reads later
+  // batches' again where they are used.
+  float lb0[8], rb0[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t j = q + u * kWR;
+    lb0[u] = j < n && nonempty(j) ? lse_part[idx(j)] : -INFINITY;
+    rb0[u] = j < n && l_part != nullptr ? l_part[idx(j)] : 1.f;
+  }
   float mq = -INFINITY;   // max of this wavefront's log-sum-exps
-  for (int64_t j0 = q; j0 < n; j0 += 8 * kWR) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) mq = fmaxf(mq, lb0[u]);
+  for (int64_t j0 = q + 8 * kWR; j0 < n; j0 += 8 * kWR) {
     float lb[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t j = j0 + u * kWR;
-      lb[u] = j < n ? lse_part[idx(j)] : -INFINITY;
+      lb[u] = j < n && nonempty(j) ? lse_part[idx(j)] : -INFINITY;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t j = j0 + u * kWR;
-      if (j < n && nonempty(j)) mq = fmaxf(mq, lb[u]);
-    }
+    for (int u = 0; u < 8; ++u) mq = fmaxf(mq, lb[u]);
   }
   float sq = 0.f;   // sum of exp(lse_j - m_q) over this wavefront's ranges
 
@@ -149,7 +157,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     const bool act = c0 < d_c;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int64_t j0 = q; j0 < n && mq != -INFINITY; j0 += 8 * kWR) {
-      if (cb > 0 || j0 > q) {   // later batches: load now
+      const bool first = j0 == q;
+      if (cb > 0 || !first) {   // later batches: load now
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int64_t j = j0 + u * kWR;
@@ -158,17 +167,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
         }
       }
       float lb[8], rb[8];
+      if (first) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t j = j0 + u * kWR;
-        lb[u] = j < n ? lse_part[idx(j)] : -INFINITY;
-        rb[u] = j < n && l_part != nullptr ? l_part[idx(j)] : 1.f;
+        for (int u = 0; u < 8; ++u) { lb[u] = lb0[u]; rb[u] = rb0[u]; }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t j = j0 + u * kWR;
+          lb[u] = j < n && nonempty(j) ? lse_part[idx(j)] : -INFINITY;
+          rb[u] = j < n && l_part != nullptr ? l_part[idx(j)] : 1.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t j = j0 + u * kWR;
-        if (j >= n) break;
-        if (!nonempty(j) || lb[u] == -INFINITY) continue;
+        if (lb[u] == -INFINITY) continue;
         const float e = expf(lb[u] - mq);
         if (cb == 0) sq += e;
         const float w = e / rb[u];
@@ -236,9 +248,14 @@ template <typename PT, int OT>
 void launch_combine_t(const DecodeArgs& a, const PT* op, hipStream_t st) {
   const int B = a.d->batch, rows = a.p->rows;
   const int64_t pairs = static_cast<int64_t>(B) * rows;
-  // ranges per sequence on average: more wavefronts per row when there are many
+  // ranges per sequence (at most): more wavefronts per row when a row has
+  // more than one batch of eight, as long as the grid still fits the chip in
+  // one round (about 28 resident wavefronts per CU)
   const int64_t per_seq = (a.p->G + B - 1) / B + 1;
-  const int wr = per_seq > 16 ? 4 : per_seq > 8 ? 2 : 1;
+  const int64_t resident = static_cast<int64_t>(kNumCUs) * 28;
+  int wr = 1;
+  if (per_seq > 16 && pairs * 4 <= resident) wr = 4;
+  else if (per_seq > 8 && pairs * 2 <= resident) wr = 2;
   const dim3 block(256), grid(static_cast<unsigned>((pairs * wr + 3) / 4));
   if (wr == 4)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 4>), grid, block, 0, st, a.page_start, op, a.lse_part,

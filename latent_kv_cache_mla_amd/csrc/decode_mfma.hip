@@ -811,7 +811,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // into LDS straight from the accumulation registers (no vector-ALU work),
     // then reads it back two rows per instruction and writes coalesced rows.
     // The combine divides by the row sum (l_part), which saves the 256
-    // per-lane multiplications a normalisation here would cost.
+    // per-lane multiplications a normalisation here would cost. The partial
+    // is written with non-temporal stores: it is read once, by the combine.
     // LDS rows are 528 bytes (128 fp32 + 16): the 16 rows of a write
     // instruction's lane group then fall in distinct bank groups.
     const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
@@ -855,12 +856,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           const bf16x2 hi = {static_cast<__bf16>(ev[s2][2]), static_cast<__bf16>(ev[s2][3])};
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
           const u32x2 u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          *reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff) = u;
+          __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff));
         }
       } else {
         float* ob = static_cast<float*>(o_part) + row0 * kDc + 128 * qq;
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) *reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff) = ev[s2];
+        for (int s2 = 0; s2 < 16; ++s2)
+          __builtin_nontemporal_store(ev[s2], reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff));
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);      // the reads are done before the next pass
       __builtin_amdgcn_wave_barrier();
