@@ -680,6 +680,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         else if (kc == 35) mfma_s_last(sn, kf[kc % (kD + 1)], qf[kc]);
         else mfma_s(sn, kf[kc % (kD + 1)], qf[kc]);
         smb_slot(kc);
+        // the weighted sum's first value fragments (its stage has been
+        // complete since the previous step), so that its first MFMA does not
+        // wait for an LDS read
+        if (kc == 31) {
+#pragma unroll
+          for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
+        }
         if constexpr (kFp8) {
           if ((kc & 3) == 2 && kc < 24 && copy)
             copy_part_f8(kc >> 2, csrc, ssrc, cnv, stg0 + ((k + 2) & 1) * kF8Stage, w, tid_s & 63);
@@ -718,8 +725,6 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         }
       };
       // ---- ... interleaved with O^T += V^T P^T over chunk k - 1 ----
-#pragma unroll
-      for (int j = 0; j < kV; ++j) vf[j] = vfrag(j);
 #pragma unroll
       for (int st = 0; st < 32; ++st) {
         if (st + kV < 32) vf[(st + kV) % (kV + 1)] = vfrag(st + kV);
