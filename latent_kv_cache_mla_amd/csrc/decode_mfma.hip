@@ -579,9 +579,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // zero probabilities of the empty chunk -1, and step n multiplies a stage
     // whose scores the mask removes entirely.
     // pg: page id of chunk k + 2, which the step copies. Its scalar load is
-    // issued before the barrier that opens the step and used at the top of
-    // the step, before any LDS read: a scalar load still in flight makes the
-    // compiler wait for every LDS read in flight at its next LDS wait.
+    // issued in the previous step's last weighted-sum MFMAs (whose LDS waits
+    // are full waits anyway) and used at the top of the step, before any LDS
+    // read: a scalar load still in flight elsewhere would make the compiler
+    // wait for every LDS read in flight at its next LDS wait.
+    int pg_next = 0;   // page id of the chunk the next step copies (chunk k + 3)
     auto step = [&](int k, int pg) {
       const uint32_t bq = stage_of(k);
       const uint32_t bv = k == 0 ? bq : stage_of(k + kS - 1);
@@ -731,6 +733,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % (kV + 1)], pf[st >> 4],
                                                                o[st & 15], 0, 0, 0);
         sma_slot(st);
+        // next step's page id: a scalar load here only joins the full LDS
+        // waits of the last MFMAs
+        if (st == 27) pg_next = k + 3 < n ? chunk_page(k + 3) : 0;
         if constexpr (kFp8) {
           if (dq) {
             if (st == 0) dq_load(k + 1, tid_s);
@@ -777,8 +782,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // raise a flag at the end of the pass; then the piece restarts in place
     // from its first chunk with the raised maxima (every wave sees the same
     // flags, so all restart together).
+    pg_next = n > 2 ? chunk_page(2) : 0;
     for (int k = 0; k <= n; ++k) {
-      const int pg = k + 2 < n ? chunk_page(k + 2) : 0;
+      const int pg = pg_next;
       if constexpr (kFp8) {
         // chunk k was dequantised in the previous step (or the prologue);
         // chunk k + 1 must have landed in its staging buffer
@@ -805,6 +811,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           clear_prev();
           raise = false;
           start();
+          pg_next = n > 2 ? chunk_page(2) : 0;
           k = -1;
         }
       }
