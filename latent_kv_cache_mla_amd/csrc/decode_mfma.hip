@@ -500,31 +500,38 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           db + kChunkContent + t * 128 + ((gq ^ swz_rope(t)) << 4))) = r4;
     };
     // The same dequantisation in pieces, for the pipeline step: dq_load
-    // issues the LDS reads of the thread's 64 codes and its scale and copies
-    // the rope unit; dq_part(j), j = 0..15, converts 4 codes and stores a
-    // 16-byte unit after every second part.
+    // issues the LDS reads of the thread's first 16 codes and its scale and
+    // copies the rope unit; dq_part(j), j = 0..15, converts 4 codes and stores
+    // a 16-byte unit after every second part. Work split (free of LDS bank
+    // conflicts for reads and writes): the 16 lanes of group g = tid / 16 take
+    // tokens T = (g % 4) + 8 (g / 4) and T + 4 (lanes 8..15), and in
+    // iteration i the 16-code units u = 8 ((i + sub) % 4) + lane % 8, sub =
+    // lane / 8 % 2: the two tokens' reads fall in opposite halves of the
+    // banks, and their stage swizzles differ in the lowest bit.
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     u32x4_t dq_c[2], dq_o;   // codes of the current and the next 16-code group
     float dq_s = 0.f;
+    auto dq_token = [](int tid) { return (((tid >> 4) & 3) + 8 * (tid >> 6)) + 4 * ((tid >> 3) & 1); };
+    auto dq_unit = [](int tid, int i) { return 8 * ((i + ((tid >> 3) & 1)) & 3) + (tid & 7); };
     auto dq_codes = [&](int q, int i, int tid) {
-      const int t = tid >> 3, gq = tid & 7;
       dq_c[i & 1] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-          static_cast<uintptr_t>(stg0 + (q & 1) * kF8Stage + t * kDc + gq * 64 + i * 16));
+          static_cast<uintptr_t>(stg0 + (q & 1) * kF8Stage + dq_token(tid) * kDc + dq_unit(tid, i) * 16));
     };
     auto dq_load = [&](int q, int tid) {
       const int t = tid >> 3, gq = tid & 7;
       const uint32_t sb = stg0 + (q & 1) * kF8Stage;
       dq_codes(q, 0, tid);
+      const int tt = dq_token(tid);
       dq_s = *reinterpret_cast<const __attribute__((address_space(3))) float*>(
-          static_cast<uintptr_t>(sb + kF8Codes + kF8Rope + 4 * t));
-      if (t >= chunk_valid(q)) dq_s = 0.f;
+          static_cast<uintptr_t>(sb + kF8Codes + kF8Rope + 4 * tt));
+      if (tt >= chunk_valid(q)) dq_s = 0.f;
       const u32x4_t r4 = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
           static_cast<uintptr_t>(sb + kF8Codes + t * 128 + gq * 16));
       *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(
           stage_of(q) + kChunkContent + t * 128 + ((gq ^ swz_rope(t)) << 4))) = r4;
     };
     auto dq_part = [&](int q, int j, int tid) {
-      const int t = tid >> 3, gq = tid & 7;
+      const int t = dq_token(tid);
       const int i = j >> 2, h = (j >> 1) & 1, e = j & 1;
       if ((j & 3) == 0 && i < 3) dq_codes(q, i + 1, tid);   // one group ahead
       const uint32_t wd = dq_c[i & 1][2 * h + e];
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       dq_o[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
       asm volatile("" : "+v"(dq_o));
       if (e == 1) {
-        const int unit = 8 * gq + 2 * i + h;
+        const int unit = 2 * dq_unit(tid, i) + h;
         *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(static_cast<uintptr_t>(
             stage_of(q) + t * 1024 + ((unit ^ swz(t)) << 4))) = dq_o;
       }
