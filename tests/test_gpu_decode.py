@@ -73,13 +73,29 @@ def test_full_size_configs(name):
         _check(inp, o, lse, f"{name}-full")
 
 
-@pytest.mark.parametrize("parts", [1, 2, 7, 0])
+@pytest.mark.parametrize("parts", [1, 2, 7, 20, 0])
 def test_split_count_invariance(parts):
+    """Results do not depend on the number of page ranges. With 2 sequences of
+    24 pages: 1, 2 and 7 ranges merge with one wavefront per row, 20 with two
+    (more than 8 ranges per sequence) and the automatic 48 with four."""
     cfg = wl.scaled(C["c2"], batch=2, seq_len=1500)
     H.say(f"case split-invariance parts={parts}")
     inp = wl.make_decode_inputs(cfg, q_mult=27.7)
     o, lse = H.run_decode(inp, num_partitions=parts)
     _check(inp, o, lse, f"parts={parts}")
+
+
+@pytest.mark.parametrize("base", ["c2", "c5"])
+def test_fp32_output_on_the_matrix_core_path(base):
+    """fp32 output: the matrix-core kernel then keeps fp32 unnormalised partials
+    (with their row sums) and the combine writes fp32."""
+    cfg = wl.scaled(SMALL[base], out_dtype="fp32")
+    H.say(f"case fp32 output on {base}-reduced")
+    inp = wl.make_decode_inputs(cfg)
+    o, lse = H.run_decode(inp)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, _kind(cfg), f"fp32out-{base}")
+    H.assert_lse_close(lse, rl, 2e-3, f"fp32out-{base}")
 
 
 def test_page_permutation_is_bitwise_invariant():
