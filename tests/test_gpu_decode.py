@@ -98,6 +98,21 @@ def test_fp32_output_on_the_matrix_core_path(base):
     H.assert_lse_close(lse, rl, 2e-3, f"fp32out-{base}")
 
 
+@pytest.mark.parametrize("n_h,q_len,dtype", [(64, 2, "bf16"), (16, 8, "bf16"), (32, 4, "fp8")])
+def test_row_groups_spanning_several_query_tokens(n_h, q_len, dtype):
+    """Fewer than 128 heads: a 128-row group of the matrix-core kernel holds
+    several query tokens, so the causal limit differs between the lanes of a
+    wavefront (including chunks that end inside the speculative window)."""
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=3, n_heads=n_h, q_len=q_len, seq_len=None, ragged=(1, 300))
+    H.say(f"case n_h={n_h} q_len={q_len} {dtype} rows={n_h * q_len}")
+    inp = wl.make_decode_inputs(cfg, seq_lens=[1 + q_len, 97, 250])
+    o, lse = H.run_decode(inp)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, _kind(cfg), f"rows-n{n_h}-q{q_len}")
+    H.assert_lse_close(lse, rl, 2e-3, f"rows-n{n_h}-q{q_len}")
+
+
 def test_page_permutation_is_bitwise_invariant():
     cfg = wl.scaled(C["c2"], batch=3, seq_len=333)
     H.say("case page-permutation")
