@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # dense bf16 matrix peak
+RIDGE_BF16 = BF16_MFMA_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)   # flop per byte
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_counters.json")
 
 WORKLOAD_TEXT = {
@@ -111,6 +112,8 @@ def main():
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for 600 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--fp8-math", action="store_true",
+                    help="fp8 cache: scores on the fp8 matrix cores (MLA_DECODE_FP8_MATH)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB three times (untimed), "
                          "so that hardware byte counters can be scaled against a known size")
@@ -134,8 +137,12 @@ def main():
     caches = [dev["cache"]] + [dev["cache"].clone() for _ in range(rotate - 1)]
     qas = [dev["q_abs"]] + [dev["q_abs"].clone() for _ in range(rotate - 1)]
     qrs = [dev["q_rope"]] + [dev["q_rope"].clone() for _ in range(rotate - 1)]
+    flags = mla.MLA_DECODE_FP8_MATH if args.fp8_math else 0
+    if args.fp8_math and cfg.cache_dtype != "fp8":
+        print("--fp8-math applies to the fp8 workload (c5) only", file=sys.stderr)
+        sys.exit(2)
     desc = mla.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
-                           cfg.cache_dtype, "bf16", cfg.out_dtype)
+                           cfg.cache_dtype, "bf16", cfg.out_dtype, flags=flags)
     ws = torch.empty(mla.mla_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
     odt = torch.float32 if cfg.out_dtype == "fp32" else torch.bfloat16
     outs = [torch.empty((cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c), dtype=odt, device="cuda")
@@ -161,7 +168,7 @@ def main():
 
     # the dominant kernel alone: split-KV decode with the plan already built
     pdesc = mla.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
-                            cfg.cache_dtype, "bf16", cfg.out_dtype, plan_ready=1)
+                            cfg.cache_dtype, "bf16", cfg.out_dtype, plan_ready=1, flags=flags)
     mla.mla_decode_plan(desc, dev["seq_lens"], ws)
 
     def part(i):
@@ -188,7 +195,7 @@ def main():
     if os.path.exists(COUNTERS_FILE):
         with open(COUNTERS_FILE) as f:
             cnt = json.load(f)
-        rec = cnt.get(args.config)
+        rec = cnt.get(args.config + ("+fp8math" if args.fp8_math else ""))
         if rec and rec.get("kernel_source_hash") == kernel_source_hash():
             traffic = rec.get("hbm_bytes_per_launch")
 
@@ -209,7 +216,7 @@ def main():
                    "seq_len": cfg.seq_len if cfg.seq_len else "ragged", "q_len": cfg.q_len,
                    "n_heads": cfg.n_heads, "d_c": cfg.d_c, "d_rope": cfg.d_rope,
                    "cache_bytes": cache_bytes, "flops": flops, "buffer_sets": rotate,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "fp8_math": bool(args.fp8_math)},
         "tflops": round(tfs, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "pct_bf16_mfma_peak": round(100 * tfs / BF16_MFMA_PEAK_TFS, 2),
@@ -218,6 +225,18 @@ def main():
                      "traffic": traffic, "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes_per_launch": cache_bytes},
     }
+    if flops / cache_bytes > RIDGE_BF16:
+        # above the bf16 ridge point (the fp8 workload: two query rows per
+        # head and 644 bytes per token) the matrix cores bound the kernel; it
+        # is priced at the dense bf16 peak in both fp8 modes (with the fp8
+        # flag the score products run at the fp8 rate, whose peak is twice
+        # that, and the weighted sum stays bf16)
+        k_tfs = flops / (kern_ms * 1e-3) / 1e12
+        line["roofline"].update({"bound": "mfma", "achieved": round(k_tfs, 2),
+                                 "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                                 "frac": round(k_tfs / BF16_MFMA_PEAK_TFS, 4),
+                                 "algorithmic_flops_per_launch": flops,
+                                 "hbm_achieved_gbs": round(k_gbs, 2)})
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")

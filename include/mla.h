@@ -76,7 +76,21 @@ typedef struct mla_decode_desc {
                                  batch's concatenated pages are cut into (split-KV) */
   int32_t plan_ready;         /* non-zero: the workspace already holds the plan that
                                  mla_decode_plan wrote for these seq_lens */
+  int32_t flags;              /* 0, or MLA_DECODE_FP8_MATH */
 } mla_decode_desc;
+
+/* flags bit: with an FP8_E4M3 cache, d_c = 512, d_rope = 64, bf16 queries and
+ * q_len * n_heads a multiple of 128, compute the content scores on the fp8
+ * matrix cores: the cached e4m3 codes are multiplied as stored against the
+ * queries rounded to e4m3 (round to nearest even) after scaling each block of
+ * 32 consecutive q_abs lanes by a power of two that puts its largest
+ * magnitude in [128, 256); the rope part and the weighted sum stay in bf16
+ * (the codes are widened exactly) with fp32 accumulation. This trades the
+ * query's rounding to 3 mantissa bits for about half the matrix-core time of
+ * the scores and no dequantisation pass. With any other cache type or shape
+ * the flag has no effect. With it, batches above 256 sequences use the plan
+ * kernel (one more launch) instead of forming the plan in the decode kernel. */
+#define MLA_DECODE_FP8_MATH 1
 
 /* Bytes of device workspace mla_decode needs for `d` (plan + split partials).
  * Pure host function; returns 0 if `d` is invalid (see mla_last_error). */

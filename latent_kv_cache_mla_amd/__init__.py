@@ -32,6 +32,7 @@ MLA_ERR_BAD_CONTENTS = 6
 MLA_FP32, MLA_BF16, MLA_FP8_E4M3 = 0, 1, 2
 MLA_PROJ_MERGED, MLA_PROJ_TWO_STAGE = 0, 1
 MLA_PAGE_SIZE = 64
+MLA_DECODE_FP8_MATH = 1
 
 DTYPE_CODES = {"fp32": MLA_FP32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 
@@ -40,7 +41,7 @@ class MlaDecodeDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "q_len", "n_heads", "d_c", "d_rope", "page_size",
         "max_blocks_per_seq", "cache_dtype", "q_dtype", "out_dtype",
-        "num_partitions", "plan_ready")]
+        "num_partitions", "plan_ready", "flags")]
 
 
 class MlaError(RuntimeError):
@@ -113,11 +114,12 @@ def _dev(t, name):
 
 
 def decode_desc(batch, q_len, n_heads, d_c, d_rope, max_blocks_per_seq, cache_dtype="bf16",
-                q_dtype="bf16", out_dtype="bf16", num_partitions=0, plan_ready=0) -> MlaDecodeDesc:
+                q_dtype="bf16", out_dtype="bf16", num_partitions=0, plan_ready=0,
+                flags=0) -> MlaDecodeDesc:
     code = lambda x: DTYPE_CODES[x] if isinstance(x, str) else int(x)  # noqa: E731
     return MlaDecodeDesc(batch, q_len, n_heads, d_c, d_rope, MLA_PAGE_SIZE, max_blocks_per_seq,
                          code(cache_dtype), code(q_dtype), code(out_dtype), num_partitions,
-                         plan_ready)
+                         plan_ready, flags)
 
 
 # ----------------------------------------------------------------------------

@@ -47,6 +47,8 @@ mla_status make_plan(const mla_decode_desc* d, DecodePlan* p) {
   if (d->out_dtype != MLA_FP32 && d->out_dtype != MLA_BF16)
     return fail(MLA_ERR_INVALID_ARGUMENT, "out_dtype must be MLA_FP32 or MLA_BF16");
   if (d->num_partitions < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "num_partitions < 0");
+  if ((d->flags & ~MLA_DECODE_FP8_MATH) != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", static_cast<unsigned>(d->flags));
   const int64_t rows = static_cast<int64_t>(d->q_len) * d->n_heads;
   if (rows > (1 << 20)) return fail(MLA_ERR_UNSUPPORTED, "q_len * n_heads too large");
   if (static_cast<int64_t>(d->batch) * d->max_blocks_per_seq > (1LL << 30))

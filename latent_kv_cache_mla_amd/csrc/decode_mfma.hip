@@ -85,6 +85,16 @@ constexpr int kF8Rope = kChunk * 2 * kDr;            // 4 KB of rope lanes per c
 constexpr int kF8Stage = kF8Codes + kF8Rope + kChunk * 4;
 constexpr int kF8Stages = 3;
 constexpr int kF8CopiesPerChunk = 6;
+// fp8 cache on the fp8 matrix cores: chunks land in a ring of four stages
+// that hold the codes as stored (32 rows of 512 bytes, XOR-swizzled in
+// 16-byte units), the 32 bf16 rope rows and the 32 token scales. Nothing is
+// dequantised in LDS: the scores multiply the codes as they are, and the
+// weighted sum converts them to bf16 in registers.
+constexpr int kF8MRope = kChunk * kDc;                    // rope rows at 16 KB
+constexpr int kF8MScales = kF8MRope + kChunk * 2 * kDr;   // token scales at 20 KB
+constexpr int kF8MStage = 20992;   // 20608 bytes used; a multiple of 512 (fragment XORs)
+constexpr int kF8MStages = 4;
+constexpr int kF8MCopies = 6;      // copy instructions per wave and chunk
 constexpr int kRowBytes = 2 * (kDc + kDr);           // one cached token, bf16
 constexpr float kRescaleLog2 = 8.0f;                 // lazy-rescale threshold (2^8)
 
@@ -121,6 +131,43 @@ __device__ __forceinline__ void mfma_s_last(f32x16& s, const bf16x8& a, const bf
 }
 // the same for the 8 chunks of a rope row (128-byte rows)
 __device__ __forceinline__ int swz_rope(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+
+// 16-byte unit swizzle of an fp8 code row (512 bytes), a function of the
+// token's low 4 bits: bijective over 16 consecutive tokens (score reads, one
+// unit per lane), and over each 8-token set of a transposed value read
+// ({0-3, 8-11} or {4-7, 12-15} plus two adjacent units), for the 32-bank and
+// the 64-bank model alike (checked by enumeration).
+__device__ __forceinline__ int swz8(int t) {
+  return (((t & 3) << 1) | ((t >> 2) & 1)) ^ (((t >> 3) & 1) * 9);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Score MFMA on the fp8 matrix cores, S += A B with S in vector registers:
+// A = 32 tokens x 64 lanes of e4m3 codes (scale 1: `one` holds the E8M0 byte
+// 127), B = 64 lanes x 32 query rows of e4m3 queries whose two 32-lane
+// blocks carry E8M0 scales in byte `sel` of `qs` (lane i gives the first
+// block's scale of row i, lane 32 + i the second's). Each lane's bytes 0..15
+// belong to the first block and 16..31 to the second.
+__device__ __forceinline__ void mfma8_s(bool first, int sel, f32x16& s, const i32x8& a,
+                                        const i32x8& b, int one, int qs) {
+#define MLA_F8(SEL)                                                                        \
+  if (first)                                                                               \
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 " SEL             \
+                 : "=&v"(s) : "v"(a), "v"(b), "v"(one), "v"(qs));                           \
+  else                                                                                     \
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 " SEL            \
+                 : "+v"(s) : "v"(a), "v"(b), "v"(one), "v"(qs));
+  switch (sel) {
+    case 0: MLA_F8("op_sel_hi:[0,0,0]") break;
+    case 1: MLA_F8("op_sel:[0,1,0] op_sel_hi:[0,0,0]") break;
+    case 2: MLA_F8("op_sel_hi:[0,1,0]") break;
+    default: MLA_F8("op_sel:[0,1,0] op_sel_hi:[0,1,0]") break;
+  }
+#undef MLA_F8
+}
 
 // One 16-byte-per-lane global -> LDS copy: lane i's 16 bytes from
 // sbase + voff land at LDS address lds + 16 i. Issued as a single instruction
@@ -206,6 +253,46 @@ __device__ __forceinline__ void copy_part_f8(int i, const uint8_t* src, const ui
   }
 }
 
+// Copy instruction i (0..5) of an fp8 chunk into its matrix-core stage at
+// `stg`: instructions 0..3 copy the code rows of tokens 8 w + 2 i and
+// 8 w + 2 i + 1 (each 16-byte unit to its swizzled place), 4 the wave's 8
+// rope rows, 5 the wave's 8 scales (two lanes). `src` is the chunk's first
+// cached row, `ssrc` its first scale; rows past n_valid are read from row 0
+// (their scales are never used).
+__device__ __forceinline__ void copy_part_f8m(int i, const uint8_t* src, const uint8_t* ssrc,
+                                              int n_valid, uint32_t stg, int w, int lane) {
+  if (i < 4) {
+    const int t = 8 * w + 2 * i + (lane >> 5);
+    const int ts = t < n_valid ? t : 0;
+    lds_dma16(src, ts * kF8Row + (((lane & 31) ^ swz8(t)) << 4), stg + (4 * w + i) * 1024);
+  } else if (i == 4) {
+    const int t = 8 * w + (lane >> 3);
+    const int ts = t < n_valid ? t : 0;
+    lds_dma16(src, ts * kF8Row + kDc + (((lane & 7) ^ swz_rope(t)) << 4), stg + kF8MRope + w * 1024);
+  } else if (lane < 2) {
+    lds_dma16(ssrc, (8 * w + 4 * lane) * 4, stg + kF8MScales + w * 32);
+  }
+}
+
+// Per-lane source offsets of a full fp8 chunk's copies into a matrix-core
+// stage (copy_part_f8m with every row valid), precomputed once.
+struct F8MCopyPlan {
+  uint32_t code[4];   // instruction i, from the row of token 8 w + 2 i
+  uint32_t rope;      // the rope copy, from the row of token 8 w
+};
+
+__device__ __forceinline__ F8MCopyPlan f8m_copy_plan(int w, int lane) {
+  F8MCopyPlan c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 8 * w + 2 * i + (lane >> 5);
+    c.code[i] = (lane >> 5) * kF8Row + (((lane & 31) ^ swz8(t)) << 4);
+  }
+  const int t = 8 * w + (lane >> 3);
+  c.rope = (lane >> 3) * kF8Row + kDc + (((lane & 7) ^ swz_rope(t)) << 4);
+  return c;
+}
+
 // s_waitcnt with vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 #define MLA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -228,23 +315,36 @@ __device__ __forceinline__ uint32_t lane_now() {
 // compiler reads the read-only tables with scalar loads.
 //
 // kLdsPlan: every workgroup forms the page prefix sums itself in LDS (batch
-// up to kMaxLdsBatch), and workgroup 0 also stores them for the combine;
-// otherwise they come from the plan kernel through page_start.
+// up to kMaxLdsBatch, or kF8MMaxLdsBatch for the fp8 matrix-core mode, whose
+// query staging leaves less LDS), and workgroup 0 also stores them for the
+// combine; otherwise they come from the plan kernel through page_start.
+//
+// kMode: 0 = bf16 cache; 1 = fp8 cache dequantised to bf16 in LDS (bf16
+// matrix cores throughout); 2 = fp8 cache on the fp8 matrix cores (scores
+// from the codes as stored against e4m3-rounded queries; weighted sum in bf16).
 constexpr int kMaxLdsBatch = 1024;
-template <bool kLdsPlan, bool kFp8>
+constexpr int kF8MMaxLdsBatch = 256;
+template <bool kLdsPlan, int kMode>
 __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ q_rope,
     const uint8_t* __restrict__ cache, const float* __restrict__ cache_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     int32_t* __restrict__ page_start, void* __restrict__ o_part, float* __restrict__ lse_part,
     float* __restrict__ l_part, MfmaParams p) {
-  // ring of bf16 chunk stages: chunk k lives in stage k % kS (fp8: plus two
-  // staging buffers after the ring)
-  constexpr int kS = kFp8 ? kF8Stages : kStages;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kS * kChunkBytes + (kFp8 ? 2 * kF8Stage : 0)];
+  constexpr bool kFp8 = kMode == 1;   // fp8 cache, dequantised in LDS
+  constexpr bool kF8M = kMode == 2;   // fp8 cache on the fp8 matrix cores
+  // ring of chunk stages: chunk k lives in stage k % kS (fp8 dequantised: plus
+  // two staging buffers after the ring; fp8 matrix cores: plus a query
+  // staging region of 18 KB per wave)
+  constexpr int kS = kF8M ? kF8MStages : (kFp8 ? kF8Stages : kStages);
+  constexpr int kStageBytes = kF8M ? kF8MStage : kChunkBytes;
+  constexpr int kSmem = kF8M ? kS * kF8MStage + 4 * (32 * 36 * 16)
+                             : kS * kChunkBytes + (kFp8 ? 2 * kF8Stage : 0);
+  constexpr int kMaxB = kF8M ? kF8MMaxLdsBatch : kMaxLdsBatch;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
   __shared__ int restart_flag[4];   // per wave: some row raised its reference in this pass
-  __shared__ int ps_lds[kLdsPlan ? kMaxLdsBatch + 1 : 1];   // page prefix sums
-  __shared__ int lens_lds[kLdsPlan ? kMaxLdsBatch : 1];     // clamped sequence lengths
+  __shared__ int ps_lds[kLdsPlan ? kMaxB + 1 : 1];   // page prefix sums
+  __shared__ int lens_lds[kLdsPlan ? kMaxB : 1];     // clamped sequence lengths
   __shared__ int wtot_lds[4];                               // per-wave page totals
 
   const int lane = threadIdx.x & 63;
@@ -294,7 +394,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     }
     // with B = 4 * 256 no thread's sequences reach index B: the last thread
     // stores the total
-    if (t == 255 && p.B == kMaxLdsBatch) ps_lds[p.B] = run;
+    if constexpr (kMaxB == 4 * 256) {
+      if (t == 255 && p.B == kMaxB) ps_lds[p.B] = run;
+    }
     __syncthreads();
     if (blockIdx.x == 0)
       for (int bb = t; bb <= p.B; bb += 256) page_start[bb] = ps_lds[bb];
@@ -343,6 +445,25 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const int qlow = 2 * (g16 & 1) + ((s16 & 3) >> 1);
     pv_base[sec] = t * 1024 + ((qlow ^ (ht & 3)) << 4) + (s16 & 1) * 8 + ((ht >> 2) << 6);
   }
+  // fp8 matrix-core mode: score A fragment e (0, 1) of k-block kb is the
+  // 16-byte unit 4 kb + 2 e + half of token l32's code row, at
+  // f8_qb[e] ^ (64 kb); rope fragments as above but at kF8MRope; transposed
+  // value reads (ds_read_b64_tr_b8): in 16-lane group g16, source lane s16
+  // reads row p = s16 / 2, bytes 8 (s16 % 2) of unit 2 mb + (g16 & 1), where
+  // row p is token (p & 3) + 8 (p >> 2) + 4 (g16 >> 1) of a 16-token step;
+  // destination lane j then holds column j of the 8 rows
+  uint32_t f8_qb[2], f8_pv = 0;
+  {
+    const int s8 = swz8(l32);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      f8_qb[e] = l32 * kDc + 64 * (s8 >> 2) + 16 * ((2 * e + half) ^ (s8 & 3));
+    const int pr = s16 >> 1;
+    const int tau = (pr & 3) + 8 * (pr >> 2) + 4 * (g16 >> 1);
+    const int st8 = swz8(tau);
+    f8_pv = tau * kDc + 32 * (st8 >> 1) + 16 * ((g16 & 1) ^ (st8 & 1)) + 8 * (s16 & 1);
+  }
+  const uint32_t rope_base8 = kF8MRope + l32 * 128 + ((half ^ (hr & 1)) << 4) + ((hr >> 1) << 5);
   const uint32_t lds0 = lds_addr(smem);
 
   for (; b < p.B && PS(b) < pe; ++b) {
@@ -376,7 +497,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // keeps 16 consecutive rows of a fragment read in distinct bank groups.
     bf16x8 qf[36];
     constexpr int kQHalf = 32 * 36 * 16;      // one wave's half: 18 KB
-    auto q_region = [&]() { return lds0 + (kS - 2) * kChunkBytes + w * kQHalf; };
+    auto q_region = [&]() {
+      if constexpr (kF8M) return lds0 + kS * kF8MStage + w * kQHalf;
+      else return lds0 + (kS - 2) * kChunkBytes + w * kQHalf;
+    };
     auto q_copy = [&](int H) {
       const int64_t qrow0 = static_cast<int64_t>(b) * p.rows + rg * kMfmaRows + w * 32;
       const uint8_t* qa = reinterpret_cast<const uint8_t*>(q_abs + qrow0 * kDc);
@@ -386,7 +510,11 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
 #pragma unroll
       for (int i = 0; i < 18; ++i) {
         const uint32_t sl = 64 * i + li, n = sl / 36, x = sl % 36;
-        const uint32_t u = 36 * H + (x ^ ((n >> 2) & 3));
+        uint32_t u = 36 * H + (x ^ ((n >> 2) & 3));
+        if constexpr (kF8M) {   // see q_read8
+          const uint32_t y = x ^ ((n >> 2) & 3);
+          u = y < 32 ? 32 * H + y : 64 + 4 * H + (y - 32);
+        }
         const uint8_t* src = u < 64 ? qa + n * (2 * kDc) + 16 * u : qr + n * (2 * kDr) + 16 * (u - 64);
         lds_dma16_va(src, reg + 1024 * i);
       }
@@ -400,6 +528,75 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       for (int kc = 0; kc < 18; ++kc)
         qf[18 * H + kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             static_cast<uintptr_t>(((kc & 1) ? r1 : r0) + 64 * (kc >> 1)));
+    };
+    // fp8 matrix-core mode: the queries as B fragments of the fp8 score
+    // MFMA. Half H of a row is q_abs units [32 H, 32 H + 32) and rope units
+    // 64 + [4 H, 4 H + 4) (units of 8 bf16): slot x of the half holds unit
+    // 32 H + x below 32, 64 + 4 H + x - 32 above. Fragment kb of lane
+    // (half, l32) holds lanes 64 kb + 16 half + (0..15) of row l32 in bytes
+    // 0..15 (the k-block's first 32-lane block) and lanes 64 kb + 32 +
+    // 16 half + (0..15) in bytes 16..31 (its second block), the same order as
+    // the code fragments. Each block is scaled by a power of two that puts its
+    // largest magnitude in [128, 256) and rounded to e4m3 (to nearest even);
+    // byte kb % 4 of qs8[kb / 4] holds the E8M0 scale of the lane's block
+    // (its half), which the MFMA applies.
+    i32x8 qf8[8];
+    int qs8[2] = {0, 0};
+    bf16x8 qr8[4];
+    auto q_read8 = [&](int H) {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const uint32_t li = lane_now();
+      const uint32_t nn = li & 31, hl = li >> 5, sw = (nn >> 2) & 3;
+      const uint32_t reg = q_region() + 576 * nn;
+      const uint32_t neg = p.neg_q ? 0x80808080u : 0u;
+      auto rd = [&](uint32_t y) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+            static_cast<uintptr_t>(reg + 16 * (y ^ sw)));
+      };
+#pragma unroll
+      for (int kbl = 0; kbl < 4; ++kbl) {
+        const u32x4 v0 = rd(8 * kbl + 2 * hl), v1 = rd(8 * kbl + 2 * hl + 1);
+        const u32x4 v2 = rd(8 * kbl + 4 + 2 * hl), v3 = rd(8 * kbl + 5 + 2 * hl);
+        const uint32_t wv[16] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3],
+                                 v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]};
+        // block maxima of |q| on the bf16 patterns (sign cleared, the integer
+        // order is the magnitude order), then across the wave halves
+        uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          a0 = max(a0, max(wv[i] & 0x7FFFu, (wv[i] >> 16) & 0x7FFFu));
+          a1 = max(a1, max(wv[8 + i] & 0x7FFFu, (wv[8 + i] >> 16) & 0x7FFFu));
+        }
+        const uint32_t pk = a0 | (a1 << 16);
+        const auto xs = __builtin_amdgcn_permlane32_swap(pk, pk, false, false);
+        const uint32_t b0 = max(xs[0] & 0xFFFFu, xs[1] & 0xFFFFu);
+        const uint32_t b1 = max(xs[0] >> 16, xs[1] >> 16);
+        // E8M0 byte e = E - 7 for a block maximum with biased exponent E (at
+        // least 1): the block divided by 2^(e - 127) has its maximum in
+        // [128, 256), below the e4m3 maximum 448
+        const int e0 = max(static_cast<int>(b0 >> 7) - 7, 1);
+        const int e1 = max(static_cast<int>(b1 >> 7) - 7, 1);
+        const float m0 = __uint_as_float(static_cast<uint32_t>(254 - e0) << 23);
+        const float m1 = __uint_as_float(static_cast<uint32_t>(254 - e1) << 23);
+        i32x8 f;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const float mult = d < 4 ? m0 : m1;
+          const uint32_t lo = wv[2 * d], hi = wv[2 * d + 1];
+          int r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(lo << 16) * mult,
+                                                  __uint_as_float(lo & 0xFFFF0000u) * mult, 0, false);
+          r = __builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(hi << 16) * mult,
+                                              __uint_as_float(hi & 0xFFFF0000u) * mult, r, true);
+          f[d] = static_cast<int>(static_cast<uint32_t>(r) ^ neg);
+        }
+        qf8[4 * H + kbl] = f;
+        qs8[H] |= (hl ? e1 : e0) << (8 * kbl);
+      }
+#pragma unroll
+      for (int kkl = 0; kkl < 2; ++kkl) {
+        const u32x4 r4 = rd(32 + 2 * kkl + hl) ^ (p.neg_q ? 0x80008000u : 0u);
+        qr8[2 * H + kkl] = __builtin_bit_cast(bf16x8, r4);
+      }
     };
     auto negate_q = [&]() {   // c s with c < 0 equals |c| (-s), and negating bf16 is exact
 #pragma unroll
@@ -425,13 +622,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       l_lane = 0.f;
     };
     // first cached row of chunk q of the piece (the page id is a scalar load)
-    constexpr int kRow = kFp8 ? kF8Row : kRowBytes;
+    constexpr int kRow = (kFp8 || kF8M) ? kF8Row : kRowBytes;   // bytes per cached row in HBM
     auto chunk_page = [&](int q) -> int { return bt[pidx0 + (q >> 1)]; };
     auto chunk_src = [&](int q) {
       return cache + chunk_page(q) * (64LL * kRow) + (q & 1) * (kChunk * kRow);
     };
     auto chunk_valid = [&](int q) { return min(kChunk, tok1 - tok0 - kChunk * q); };
-    auto stage_of = [&](int q) { return lds0 + (static_cast<uint32_t>(q) % kS) * kChunkBytes; };
+    auto stage_of = [&](int q) { return lds0 + (static_cast<uint32_t>(q) % kS) * kStageBytes; };
     const uint32_t stg0 = lds0 + kS * kChunkBytes;   // fp8 staging buffers
     // copy all of chunk q at once (into its stage, or for fp8 its staging buffer)
     // (the per-lane offsets are formed afresh: see lane_now)
@@ -439,7 +636,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       const uint8_t* src = chunk_src(q);
       const int nv = chunk_valid(q);
       const int li = static_cast<int>(lane_now());
-      if constexpr (kFp8) {
+      if constexpr (kF8M) {
+        const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
+            cache_scale + static_cast<int64_t>(chunk_page(q)) * 64 + (q & 1) * kChunk);
+#pragma unroll
+        for (int i = 0; i < kF8MCopies; ++i) copy_part_f8m(i, src, ssrc, nv, stage_of(q), w, li);
+      } else if constexpr (kFp8) {
         const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
             cache_scale + static_cast<int64_t>(chunk_page(q)) * 64 + (q & 1) * kChunk);
 #pragma unroll
@@ -559,16 +761,21 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         __syncthreads();
         dequant(0);
       } else {
-        if (n > 1) MLA_WAIT_VM(kCopiesPerChunk);
+        constexpr int kC = kF8M ? kF8MCopies : kCopiesPerChunk;
+        if (n > 1) MLA_WAIT_VM(kC);
         else MLA_WAIT_VM(0);
       }
     };
 
     float m_prev = 0.f;      // reference of the previous chunk's probabilities
     f32x16 sp;               // raw (masked) scores of the previous chunk
+    f32x16 scl_prev;         // (fp8 matrix cores) its token scales, zero past its valid rows
     auto clear_prev = [&]() {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sp[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        sp[r] = -INFINITY;
+        scl_prev[r] = 0.f;
+      }
       m_prev = 0.f;
     };
     bool raise = false;      // some row of this lane crossed the lazy threshold in this pass
@@ -755,6 +962,179 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       m_prev = m_run == -INFINITY ? 0.f : m_run;
     };
 
+    // ---- fp8 matrix-core mode: one pipeline step k ----
+    //   phase 1: scores of chunk k: 8 fp8 MFMAs over the 512 code lanes
+    //            (codes as stored, queries e4m3 with block scales) into one
+    //            accumulator, 4 bf16 MFMAs over the 64 rope lanes into
+    //            another; interleaved with the weights of chunk k - 1
+    //            (p = 2^(c s - m), w = p s_j rounded to bf16, row sums of p)
+    //            and the copy of chunk k + 2;
+    //   phase 2: weighted sum of chunk k - 1 on the bf16 matrix cores, its
+    //            codes read transposed (ds_read_b64_tr_b8) and converted to
+    //            bf16 in registers (exact), interleaved with the scores of
+    //            chunk k (s_j times the code part plus the rope part), their
+    //            mask, the row max and the lazy reference update.
+    // The token scale is applied once per score and once per weight:
+    // c_j = s_j code_j, so s_j (q . code_j) is the content score and
+    // sum_j p_j s_j code_j the weighted sum.
+    F8MCopyPlan cp8 = f8m_copy_plan(w, static_cast<int>(lane_now()));
+    const int one127 = 127;   // E8M0 1.0: the code operand is not scaled
+    auto step8 = [&](int k, int pg) {
+      const uint32_t bq = stage_of(k);
+      const uint32_t bv = k == 0 ? bq : stage_of(k + kS - 1);
+      const bool copy = k + 2 < n;
+      const int cnv = copy ? chunk_valid(k + 2) : kChunk;
+      const int64_t pgc = pg;
+      const uint8_t* csrc = cache + pgc * (64LL * kF8Row) + ((k + 2) & 1) * (kChunk * kF8Row);
+      const uint8_t* ssrc = reinterpret_cast<const uint8_t*>(
+          cache_scale + pgc * 64 + ((k + 2) & 1) * kChunk);
+      asm volatile("" : "+s"(csrc), "+s"(ssrc));
+      const uint32_t cbuf = stage_of(k + 2);
+      const bool cfast = copy && cnv == kChunk;
+      if (copy && !cfast) issue(k + 2);
+      const uint8_t* csw = csrc + 8 * w * kF8Row;
+      uint32_t qb0 = f8_qb[0], qb1 = f8_qb[1], rb = rope_base8, vb = f8_pv;
+      asm volatile("" : "+v"(qb0), "+v"(qb1), "+v"(rb), "+v"(vb));
+      int tid_s = static_cast<int>(threadIdx.x);
+      asm volatile("" : "+v"(tid_s));
+      const uint32_t a0 = bq + qb0, a1 = bq + qb1, ar = bq + rb, av = bv + vb;
+      auto copy_fast8 = [&](int i) {
+        if (i < 4) lds_dma16(csw + 2 * i * kF8Row, cp8.code[i], cbuf + (4 * w + i) * 1024);
+        else if (i == 4) lds_dma16(csw, cp8.rope, cbuf + kF8MRope + w * 1024);
+        else if ((tid_s & 63) < 2)
+          lds_dma16(ssrc, (8 * w + 4 * (tid_s & 63)) * 4, cbuf + kF8MScales + w * 32);
+      };
+      auto kfrag8 = [&](int kb) {
+        const i32x4 lo = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+            static_cast<uintptr_t>(a0 ^ (64 * kb)));
+        const i32x4 hi = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+            static_cast<uintptr_t>(a1 ^ (64 * kb)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      auto rfrag8 = [&](int kk) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            static_cast<uintptr_t>(ar ^ (kk << 5)));
+      };
+      auto vraw8 = [&](int st) {
+        const int mb = st & 15, cc = st >> 4;
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(static_cast<uintptr_t>((av ^ (32 * mb)) + 8192 * cc)));
+      };
+      auto vcvt = [](i32x2 r) {
+        const bf16x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, false);
+        const bf16x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[0], 1.0f, true);
+        const bf16x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, false);
+        const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, true);
+        return bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
+      };
+      constexpr int kV8 = 4;   // transposed value read distance (MFMAs)
+      i32x8 kf[3];
+      bf16x8 rf[3];
+      i32x2 vr[kV8 + 1];
+      bf16x8 pf[2];
+      f32x4 scl4[4];           // token scales of chunk k (tokens 8 a + 4 half + 0..3)
+      f32x16 sc, sr;           // code and rope parts of chunk k's scores
+
+      // weights of chunk k - 1, two tokens per slot (pinned to their slot)
+      auto smb8 = [&](int j) {
+        if (j < 8) {
+          const int r = 2 * j;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sp[r], c, -m_prev));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sp[r + 1], c, -m_prev));
+          const bf16x2 two = {static_cast<__bf16>(p0 * scl_prev[r]),
+                              static_cast<__bf16>(p1 * scl_prev[r + 1])};
+          pf[r >> 3][r & 7] = two[0];
+          pf[r >> 3][(r & 7) + 1] = two[1];
+          l_lane += p0 + p1;
+          asm volatile("" : "+v"(l_lane));
+        }
+      };
+
+      // ---- phase 1 ----
+      kf[0] = kfrag8(0);
+      kf[1] = kfrag8(1);
+#pragma unroll
+      for (int j = 0; j < 12; ++j) {
+        if (j < 8) {
+          if (j + 2 < 8) kf[(j + 2) % 3] = kfrag8(j + 2);
+          else rf[(j - 6) % 3] = rfrag8(j - 6);
+          mfma8_s(j == 0, j & 3, sc, kf[j % 3], qf8[j], one127, qs8[j >> 2]);
+        } else {
+          const int kk = j - 8;
+          if (kk + 2 < 4) rf[(kk + 2) % 3] = rfrag8(kk + 2);
+          if (kk == 0) mfma_s_first(sr, rf[0], qr8[0]);
+          else if (kk == 3) mfma_s_last(sr, rf[kk % 3], qr8[kk]);
+          else mfma_s(sr, rf[kk % 3], qr8[kk]);
+        }
+        if (j == 0) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            scl4[a] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+                static_cast<uintptr_t>(bq + kF8MScales + 32 * a + 16 * half));
+        }
+        smb8(j);
+        if (j < kF8MCopies && cfast) copy_fast8(j);
+        if (j == 10) {
+#pragma unroll
+          for (int q = 0; q < kV8; ++q) vr[q] = vraw8(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- phase 2 ----
+      const bool part = tok0 + kChunk * k + kChunk > tend_all;   // wave-uniform
+      f32x16 sn;
+      float mx = -INFINITY;
+      auto sma8 = [&](int s) {
+        if (s == 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sn[r] = fmaf(sc[r], scl4[r >> 2][r & 3], sr[r]);
+          if (part) {
+            // tokens at or past the row's visible end get -inf; scales of
+            // rows past the chunk's valid rows (copied from row 0) get 0, so
+            // that their zero weights stay zero
+            const int base = tok0 + kChunk * k + 4 * half;
+            const int lim = tend - base, nvr = tok1 - base;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int idx = (r & 3) + 8 * (r >> 2);
+              sn[r] = idx < lim ? sn[r] : -INFINITY;
+              scl4[r >> 2][r & 3] = idx < nvr ? scl4[r >> 2][r & 3] : 0.f;
+            }
+          }
+        } else if (s >= 2 && s < 10) {
+          const int q = s - 2;
+          asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(sn[2 * q]), "v"(sn[2 * q + 1]));
+          asm volatile("" : "+v"(mx));
+        } else if (s == 10) {
+          const auto xs = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                           false, false);
+          mx = fmaxf(__uint_as_float(xs[0]), __uint_as_float(xs[1])) * c;
+          asm volatile("" : "+v"(mx));
+        } else if (s == 11) {
+          const bool up = mx > m_run + kRescaleLog2;
+          raise = raise || (up && m_run != -INFINITY);
+          m_run = up ? mx : m_run;
+        }
+      };
+      bf16x8 vcv[2];
+      vcv[0] = vcvt(vr[0]);
+#pragma unroll
+      for (int st = 0; st < 32; ++st) {
+        if (st + kV8 < 32) vr[(st + kV8) % (kV8 + 1)] = vraw8(st + kV8);
+        o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcv[st & 1], pf[st >> 4], o[st & 15],
+                                                              0, 0, 0);
+        if (st + 1 < 32) vcv[(st + 1) & 1] = vcvt(vr[(st + 1) % (kV8 + 1)]);
+        sma8(st);
+        if (st == 27) pg_next = k + 3 < n ? chunk_page(k + 3) : 0;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sp = sn;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scl_prev[r] = scl4[r >> 2][r & 3];
+      m_prev = m_run == -INFINITY ? 0.f : m_run;
+    };
+
     zero_o();
     clear_prev();
     __syncthreads();   // earlier reads of every stage are done
@@ -766,11 +1146,12 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     // half read into registers; the second half and chunk 1 in flight; wait
     // for all but chunk 1 (copies complete in order). The query regions are
     // the ring's last two stages, which chunks 0 and 1 do not use.
-    constexpr int kCopies = kFp8 ? kF8CopiesPerChunk : kCopiesPerChunk;
+    constexpr int kCopies = kF8M ? kF8MCopies : (kFp8 ? kF8CopiesPerChunk : kCopiesPerChunk);
     q_copy(0);
     issue(0);
     MLA_WAIT_VM(kCopies);          // this wave's first query half
-    q_read(0);
+    if constexpr (kF8M) q_read8(0);
+    else q_read(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before it is overwritten
     q_copy(1);
     if (n > 1) {
@@ -779,12 +1160,15 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     } else {
       MLA_WAIT_VM(0);
     }
-    q_read(1);
+    if constexpr (kF8M) q_read8(1);   // (negates the queries itself)
+    else q_read(1);
     if constexpr (kFp8) {
       __syncthreads();             // every wave's copies of chunk 0 have landed
       dequant(0);
     }
-    if (p.neg_q) negate_q();
+    if constexpr (!kF8M) {
+      if (p.neg_q) negate_q();
+    }
     // Chunk loop. A row whose max rose past the lazy threshold makes its wave
     // raise a flag at the end of the pass; then the piece restarts in place
     // from its first chunk with the raised maxima (every wave sees the same
@@ -802,12 +1186,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         // (which held chunk k): both were done with before the barrier
       } else {
         if (k > 0 && k < n) {
-          if (k + 1 < n) MLA_WAIT_VM(kCopiesPerChunk);   // this wave's copies of chunk k
+          if (k + 1 < n) MLA_WAIT_VM(kCopies);   // this wave's copies of chunk k
           else MLA_WAIT_VM(0);
         }
         __syncthreads();     // ... and every other wave's
       }
-      step(k, pg);
+      if constexpr (kF8M) step8(k, pg);
+      else step(k, pg);
       if (k == n) {        // end of the pass: no copy is in flight
         const bool any_raise = __any(raise);
         if (lane == 0) restart_flag[w] = any_raise ? 1 : 0;
@@ -896,7 +1281,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
 
 }  // namespace
 
-bool mfma_lds_plan(const mla_decode_desc* d) { return d->batch <= kMaxLdsBatch; }
+bool mfma_fp8_math(const mla_decode_desc* d) {
+  return d->cache_dtype == MLA_FP8_E4M3 && (d->flags & MLA_DECODE_FP8_MATH) != 0;
+}
+
+bool mfma_lds_plan(const mla_decode_desc* d) {
+  return d->batch <= (mfma_fp8_math(d) ? kF8MMaxLdsBatch : kMaxLdsBatch);
+}
 
 bool mfma_supports(const mla_decode_desc* d) {
   return d->d_c == kDc && d->d_rope == kDr &&
@@ -923,8 +1314,11 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   const int64_t g_pad = (a.p->G + 7) / 8 * 8;
   const dim3 grid(static_cast<unsigned>(g_pad * a.p->row_groups)), block(256);
   const bool lds_plan = mfma_lds_plan(d), fp8 = d->cache_dtype == MLA_FP8_E4M3;
-  auto kernel = lds_plan ? (fp8 ? decode_mfma_bf16<true, true> : decode_mfma_bf16<true, false>)
-                         : (fp8 ? decode_mfma_bf16<false, true> : decode_mfma_bf16<false, false>);
+  const int mode = fp8 ? (mfma_fp8_math(d) ? 2 : 1) : 0;
+  auto kernel = lds_plan ? (mode == 2 ? decode_mfma_bf16<true, 2>
+                            : mode == 1 ? decode_mfma_bf16<true, 1> : decode_mfma_bf16<true, 0>)
+                         : (mode == 2 ? decode_mfma_bf16<false, 2>
+                            : mode == 1 ? decode_mfma_bf16<false, 1> : decode_mfma_bf16<false, 0>);
   hipLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
                      a.cache_scale, a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start),

@@ -64,6 +64,8 @@ struct DecodeArgs {
 mla_status launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
 bool mfma_supports(const mla_decode_desc* d);
+// An fp8 cache whose descriptor asks for MLA_DECODE_FP8_MATH.
+bool mfma_fp8_math(const mla_decode_desc* d);
 // The MFMA kernel forms the page prefix sums itself (and stores them for the
 // combine), so no plan launch is needed.
 bool mfma_lds_plan(const mla_decode_desc* d);

@@ -58,15 +58,17 @@ def device_inputs(inp: wl.DecodeInputs, max_blocks: int | None = None):
 
 
 def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: bool = True,
-               plan_separately: bool = False, with_lse: bool = True, scale: float | None = None):
+               plan_separately: bool = False, with_lse: bool = True, scale: float | None = None,
+               flags: int = 0):
     """Runs mla_decode on the GPU; returns (o float64 [B,q_len,n_h,d_c], lse).
-    `scale` overrides the config's softmax scale."""
+    `scale` overrides the config's softmax scale; `flags` goes to the
+    descriptor (MLA_DECODE_FP8_MATH)."""
     m = lib()
     cfg = inp.cfg
     dev = dev or device_inputs(inp)
     q_dt = "fp32" if cfg.cache_dtype == "fp32" else "bf16"
     desc = m.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
-                         cfg.cache_dtype, q_dt, cfg.out_dtype, num_partitions)
+                         cfg.cache_dtype, q_dt, cfg.out_dtype, num_partitions, flags=flags)
     ws_bytes = m.mla_decode_workspace_size(desc)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     odt = torch.float32 if cfg.out_dtype == "fp32" else torch.bfloat16

@@ -60,7 +60,8 @@ def test_workspace_size_is_pure_and_monotone(m):
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, 1), ("q_len", 0, 1), ("n_heads", 0, 1), ("d_c", 12, 2), ("d_c", 2048, 2),
     ("d_rope", 5, 2), ("page_size", 32, 2), ("max_blocks_per_seq", 0, 1), ("cache_dtype", 9, 1),
-    ("q_dtype", 2, 1), ("out_dtype", 2, 1), ("num_partitions", -1, 1),
+    ("q_dtype", 2, 1), ("out_dtype", 2, 1), ("num_partitions", -1, 1), ("flags", 2, 1),
+    ("flags", -1, 1),
 ])
 def test_bad_descriptors_rejected(m, field, value, status):
     d = m.decode_desc(2, 1, 16, 512, 64, 4)
@@ -69,6 +70,15 @@ def test_bad_descriptors_rejected(m, field, value, status):
     r = m.lib.mla_decode(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 1.0, 16, None, 256, 1 << 30, None)
     assert r == status, m.mla_last_error()
     assert m.mla_last_error() != ""
+
+
+def test_fp8_math_flag_is_accepted_for_every_cache(m):
+    """MLA_DECODE_FP8_MATH only changes how an fp8 cache on the matrix-core
+    shape is multiplied; the workspace layout does not depend on it."""
+    for dt in ("bf16", "fp8"):
+        a = m.decode_desc(128, 2, 128, 512, 64, 128, dt)
+        b = m.decode_desc(128, 2, 128, 512, 64, 128, dt, flags=m.MLA_DECODE_FP8_MATH)
+        assert m.mla_decode_workspace_size(a) == m.mla_decode_workspace_size(b) > 0
 
 
 def test_fp32_queries_need_fp32_cache(m):
