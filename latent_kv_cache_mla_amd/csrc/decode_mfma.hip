@@ -963,22 +963,45 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     };
 
     // ---- fp8 matrix-core mode: one pipeline step k ----
+    // Scores and softmax are per row, as in the other modes: wave w owns rows
+    // 32 w .. 32 w + 31 of the group. The weighted sum is split by columns
+    // instead: wave w accumulates O^T for columns 128 w .. 128 w + 127 of all
+    // 128 rows (the same 16 accumulator tiles), so each transposed code
+    // fragment is read and widened once and multiplies the weights of all
+    // four row blocks. The weights of chunk k are exchanged through LDS: each
+    // wave stores its rows' bf16 weight fragments (in the B-operand layout)
+    // into buffer k % 2 at the end of step k, and every wave reads all four in
+    // step k + 1, after the barrier that opens it.
     //   phase 1: scores of chunk k: 8 fp8 MFMAs over the 512 code lanes
     //            (codes as stored, queries e4m3 with block scales) into one
-    //            accumulator, 4 bf16 MFMAs over the 64 rope lanes into
-    //            another; interleaved with the weights of chunk k - 1
-    //            (p = 2^(c s - m), w = p s_j rounded to bf16, row sums of p)
-    //            and the copy of chunk k + 2;
-    //   phase 2: weighted sum of chunk k - 1 on the bf16 matrix cores, its
-    //            codes read transposed (ds_read_b64_tr_b8) and converted to
-    //            bf16 in registers (exact), interleaved with the scores of
-    //            chunk k (s_j times the code part plus the rope part), their
-    //            mask, the row max and the lazy reference update.
+    //            accumulator and 4 bf16 MFMAs over the 64 rope lanes into
+    //            another, with the copy of chunk k + 2;
+    //   phase 2: weighted sum of chunk k - 1 on the bf16 matrix cores (codes
+    //            read transposed with ds_read_b64_tr_b8 and widened to bf16 in
+    //            registers, exactly), interleaved with chunk k's scores
+    //            (s_j times the code part plus the rope part), mask, row max,
+    //            lazy reference update, weights w = 2^(c s - m) s_j (rounded
+    //            to bf16; the row sum takes the unrounded 2^(c s - m)) and
+    //            their store.
     // The token scale is applied once per score and once per weight:
     // c_j = s_j code_j, so s_j (q . code_j) is the content score and
     // sum_j p_j s_j code_j the weighted sum.
     F8MCopyPlan cp8 = f8m_copy_plan(w, static_cast<int>(lane_now()));
     const int one127 = 127;   // E8M0 1.0: the code operand is not scaled
+    // weight buffers (2 x 8 KB, in the query staging region, which is idle
+    // after the prologue): buffer q, row block rb, token step cc, lane l
+    const uint32_t wbuf0 = lds0 + kS * kF8MStage;
+    auto wslot = [&](int q, int rbk, int cc) {
+      return wbuf0 + (q & 1) * 8192 + rbk * 2048 + cc * 1024 + lane_now() * 16;
+    };
+    // zero the weights of "chunk -1" (buffer 1), which step 0 multiplies
+    auto clear_w = [&]() {
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+            static_cast<uintptr_t>(wslot(1, w, cc))) = u32x4{0u, 0u, 0u, 0u};
+    };
     auto step8 = [&](int k, int pg) {
       const uint32_t bq = stage_of(k);
       const uint32_t bv = k == 0 ? bq : stage_of(k + kS - 1);
@@ -1015,8 +1038,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
             static_cast<uintptr_t>(ar ^ (kk << 5)));
       };
-      auto vraw8 = [&](int st) {
-        const int mb = st & 15, cc = st >> 4;
+      // V^T fragment g = 4 cc + mb: columns 128 w + 32 mb, tokens 16 cc ..
+      auto vraw8 = [&](int g) {
+        const int mb = 4 * w + (g & 3), cc = g >> 2;
         return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2*)(static_cast<uintptr_t>((av ^ (32 * mb)) + 8192 * cc)));
       };
@@ -1027,28 +1051,19 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
         const bf16x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[1], 1.0f, true);
         return bf16x8{e0[0], e0[1], e1[0], e1[1], e2[0], e2[1], e3[0], e3[1]};
       };
-      constexpr int kV8 = 4;   // transposed value read distance (MFMAs)
+      // weight fragment (token step cc, row block rbk) of chunk k - 1
+      auto wfrag = [&](int cc, int rbk) {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            static_cast<uintptr_t>(wslot(k + 1, rbk, cc)));
+      };
       i32x8 kf[3];
       bf16x8 rf[3];
-      i32x2 vr[kV8 + 1];
-      bf16x8 pf[2];
+      i32x2 vr[3];
+      bf16x8 va[2];
+      bf16x8 pb[8];            // weights of chunk k - 1: [cc][row block]
+      bf16x8 pw[2];            // this wave's weights of chunk k: [cc]
       f32x4 scl4[4];           // token scales of chunk k (tokens 8 a + 4 half + 0..3)
       f32x16 sc, sr;           // code and rope parts of chunk k's scores
-
-      // weights of chunk k - 1, two tokens per slot (pinned to their slot)
-      auto smb8 = [&](int j) {
-        if (j < 8) {
-          const int r = 2 * j;
-          float p0 = __builtin_amdgcn_exp2f(fmaf(sp[r], c, -m_prev));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(sp[r + 1], c, -m_prev));
-          const bf16x2 two = {static_cast<__bf16>(p0 * scl_prev[r]),
-                              static_cast<__bf16>(p1 * scl_prev[r + 1])};
-          pf[r >> 3][r & 7] = two[0];
-          pf[r >> 3][(r & 7) + 1] = two[1];
-          l_lane += p0 + p1;
-          asm volatile("" : "+v"(l_lane));
-        }
-      };
 
       // ---- phase 1 ----
       kf[0] = kfrag8(0);
@@ -1072,12 +1087,18 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
             scl4[a] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
                 static_cast<uintptr_t>(bq + kF8MScales + 32 * a + 16 * half));
         }
-        smb8(j);
         if (j < kF8MCopies && cfast) copy_fast8(j);
-        if (j == 10) {
+        // the weighted sum's first operands
+        if (j == 6) {
 #pragma unroll
-          for (int q = 0; q < kV8; ++q) vr[q] = vraw8(q);
+          for (int q = 0; q < 4; ++q) pb[q] = wfrag(0, q);
         }
+        if (j == 8) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pb[4 + q] = wfrag(1, q);
+        }
+        if (j == 9) vr[0] = vraw8(0);
+        if (j == 10) vr[1] = vraw8(1);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -1115,24 +1136,36 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           const bool up = mx > m_run + kRescaleLog2;
           raise = raise || (up && m_run != -INFINITY);
           m_run = up ? mx : m_run;
+        } else if (s >= 12 && s < 20) {
+          // weights of chunk k, two tokens per slot
+          const int r = 2 * (s - 12);
+          const float mref = m_run == -INFINITY ? 0.f : m_run;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sn[r], c, -mref));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sn[r + 1], c, -mref));
+          const bf16x2 two = {static_cast<__bf16>(p0 * scl4[r >> 2][r & 3]),
+                              static_cast<__bf16>(p1 * scl4[r >> 2][(r & 3) + 1])};
+          pw[r >> 3][r & 7] = two[0];
+          pw[r >> 3][(r & 7) + 1] = two[1];
+          l_lane += p0 + p1;
+          asm volatile("" : "+v"(l_lane));
+        } else if (s == 20 || s == 21) {
+          const int cc = s - 20;
+          *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+              static_cast<uintptr_t>(wslot(k, w, cc))) = pw[cc];
         }
       };
-      bf16x8 vcv[2];
-      vcv[0] = vcvt(vr[0]);
+      va[0] = vcvt(vr[0]);
 #pragma unroll
       for (int st = 0; st < 32; ++st) {
-        if (st + kV8 < 32) vr[(st + kV8) % (kV8 + 1)] = vraw8(st + kV8);
-        o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcv[st & 1], pf[st >> 4], o[st & 15],
-                                                              0, 0, 0);
-        if (st + 1 < 32) vcv[(st + 1) & 1] = vcvt(vr[(st + 1) % (kV8 + 1)]);
+        const int g = st >> 2, rbk = st & 3;   // code fragment, row block
+        if (rbk == 0 && g + 2 < 8) vr[(g + 2) % 3] = vraw8(g + 2);
+        o[4 * rbk + (g & 3)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            va[g & 1], pb[4 * (g >> 2) + rbk], o[4 * rbk + (g & 3)], 0, 0, 0);
+        if (rbk == 2 && g + 1 < 8) va[(g + 1) & 1] = vcvt(vr[(g + 1) % 3]);
         sma8(st);
         if (st == 27) pg_next = k + 3 < n ? chunk_page(k + 3) : 0;
         __builtin_amdgcn_sched_barrier(0);
       }
-      sp = sn;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) scl_prev[r] = scl4[r >> 2][r & 3];
-      m_prev = m_run == -INFINITY ? 0.f : m_run;
     };
 
     zero_o();
@@ -1160,8 +1193,13 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     } else {
       MLA_WAIT_VM(0);
     }
-    if constexpr (kF8M) q_read8(1);   // (negates the queries itself)
-    else q_read(1);
+    if constexpr (kF8M) {
+      q_read8(1);                  // (negates the queries itself)
+      __syncthreads();             // every wave has read its queries: the region
+      clear_w();                   // now holds the weight buffers
+    } else {
+      q_read(1);
+    }
     if constexpr (kFp8) {
       __syncthreads();             // every wave's copies of chunk 0 have landed
       dequant(0);
@@ -1202,6 +1240,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           zero_o();
           clear_prev();
           raise = false;
+          if constexpr (kF8M) clear_w();
           start();
           pg_next = n > 2 ? chunk_page(2) : 0;
           k = -1;
@@ -1226,7 +1265,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint32_t ewave = lds0 + w * 32 * kEpiRow;
     const uint32_t ewr = ewave + (li & 31) * kEpiRow + (li >> 5) * 16;   // row l32, unit half
     const uint32_t erd = ewave + (li >> 5) * kEpiRow + (li & 31) * 16;   // row li / 32, unit li % 32
-    const int64_t row0 = slot * p.rows + rg * kMfmaRows + w * 32;
+    // rows of pass qq: the wave's own 32 rows (columns 128 qq ..), or in the
+    // fp8 matrix-core mode row block qq (the wave's columns 128 w ..)
+    const int64_t rowg = slot * p.rows + rg * kMfmaRows;
     __syncthreads();                           // every wave is done with the stages
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -1252,8 +1293,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       for (int s2 = 0; s2 < 16; ++s2)
         ev[s2] = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             static_cast<uintptr_t>(erd + 2 * s2 * kEpiRow));
+      const int64_t row0 = rowg + 32 * (kF8M ? qq : w);
+      const int col0 = 128 * (kF8M ? w : qq);
       if (p.part_bf16) {
-        uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + 128 * qq;
+        uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + col0;
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2) {
           const bf16x2 lo = {static_cast<__bf16>(ev[s2][0]), static_cast<__bf16>(ev[s2][1])};
@@ -1263,7 +1306,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff));
         }
       } else {
-        float* ob = static_cast<float*>(o_part) + row0 * kDc + 128 * qq;
+        float* ob = static_cast<float*>(o_part) + row0 * kDc + col0;
 #pragma unroll
         for (int s2 = 0; s2 < 16; ++s2)
           __builtin_nontemporal_store(ev[s2], reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff));
