@@ -55,6 +55,13 @@
 //   * the LDS chunk layout is XOR-swizzled in 16-byte units so that both the
 //     row-wise score reads and the transposed value reads are free of bank
 //     conflicts.
+//   * fp8 cache (e4m3 codes, bf16 rope lanes, one fp32 scale per token), two
+//     modes: by default each chunk is dequantised into bf16 stages laid out as
+//     above, and the rest is the bf16 code; with MLA_DECODE_FP8_MATH the scores
+//     run on the fp8 matrix cores from the codes as stored, against queries
+//     rounded to e4m3 with a power-of-two scale per 32 lanes, and the weighted
+//     sum is split by columns across the wavefronts (codes widened to bf16 in
+//     registers once per workgroup, weights exchanged through LDS).
 #include <type_traits>
 
 #include "internal.h"
