@@ -211,3 +211,15 @@ def test_sharp_content_scores_error_report(variant):
           f"lse max-abs {np.max(np.abs(lse - rl)):.3e}")
     assert rf < 0.1
     H.assert_lse_close(lse, rl, _lse_tol(inp), f"f8m-{variant}")
+
+
+def test_flag_has_no_effect_on_a_bf16_cache():
+    """The flag only changes how an fp8 cache is multiplied: with a bf16
+    cache the results are bitwise those of the call without it."""
+    cfg = wl.scaled(C["c2"], batch=3, seq_len=700)
+    H.say("case fp8-math flag on a bf16 cache")
+    inp = wl.make_decode_inputs(cfg)
+    dev = H.device_inputs(inp)
+    a = H.run_decode(inp, dev=dev, flags=F8)
+    b = H.run_decode(inp, dev=dev)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
