@@ -119,7 +119,7 @@ def main():
                          "so that hardware byte counters can be scaled against a known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -165,6 +165,16 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+
+    # per-step distribution (a separate pass: an event pair around every step)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    per_step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
 
     # the dominant kernel alone: split-KV decode with the plan already built
     pdesc = mla.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
@@ -217,6 +227,7 @@ def main():
                    "n_heads": cfg.n_heads, "d_c": cfg.d_c, "d_rope": cfg.d_rope,
                    "cache_bytes": cache_bytes, "flops": flops, "buffer_sets": rotate,
                    "parallelism": "single GPU", "fp8_math": bool(args.fp8_math)},
+        "step_us_p10_p50_p90": [round(float(np.percentile(per_step_us, q)), 2) for q in (10, 50, 90)],
         "tflops": round(tfs, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "pct_bf16_mfma_peak": round(100 * tfs / BF16_MFMA_PEAK_TFS, 2),
