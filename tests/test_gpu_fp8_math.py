@@ -223,3 +223,29 @@ def test_flag_has_no_effect_on_a_bf16_cache():
     a = H.run_decode(inp, dev=dev, flags=F8)
     b = H.run_decode(inp, dev=dev)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("flags", [0, F8])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_restart_on_a_late_larger_logit(dtype, flags):
+    """One page range for the whole batch (num_partitions=1: one workgroup
+    walks both sequences), and rope needles in late chunks whose logits
+    exceed everything before them by far more than the lazy-reference
+    threshold (2^8): each sequence's pass raises its reference twice and
+    restarts, and the result must still match the oracle."""
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=2, q_len=1, seq_len=700)
+    H.say(f"case restart {dtype} flags={flags}")
+    inp = wl.make_decode_inputs(cfg)
+    inp.q_rope_bits[...] = 0
+    inp.q_rope_bits[..., 0] = wl.to_bf16_bits(np.array([1.0]))[0]
+    for b in range(cfg.batch):
+        kr = inp.krope_bits[b] if dtype == "fp8" else inp.lat_bits[b][:, cfg.d_c:]
+        for j, logit in ((300, 12.0), (650, 24.0)):   # chunks 9 and 20 of the pass
+            kr[j, :] = 0
+            kr[j, 0] = wl.to_bf16_bits(np.array([logit / cfg.softmax_scale]))[0]
+    o, lse = H.run_decode(inp, num_partitions=1, flags=flags)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, dtype, f"restart-{dtype}-{flags}")
+    tol = 2e-3 if flags == 0 or dtype == "bf16" else _lse_tol(inp)
+    H.assert_lse_close(lse, rl, tol, f"restart-{dtype}-{flags}")
