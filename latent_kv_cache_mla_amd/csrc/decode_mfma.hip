@@ -370,6 +370,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   const int64_t g = (id & 7) * G8 + jx / p.row_groups;
   const int rg = static_cast<int>(jx % p.row_groups);
   if (g >= p.G) return;
+  // rows of this group that exist (the last group of a row count that is
+  // not a multiple of 128 is padded: its missing rows load the group's first
+  // query row, are computed like the others, and are never stored)
+  const int rv = min(kMfmaRows, p.rows - rg * kMfmaRows);
   if constexpr (kLdsPlan) {
     // page_start[b] = sum_{b' < b} ceil(S_b' / 64): four sequences per thread,
     // a scan across the wavefront, then the totals of the waves before
@@ -522,7 +526,9 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
           const uint32_t y = x ^ ((n >> 2) & 3);
           u = y < 32 ? 32 * H + y : 64 + 4 * H + (y - 32);
         }
-        const uint8_t* src = u < 64 ? qa + n * (2 * kDc) + 16 * u : qr + n * (2 * kDr) + 16 * (u - 64);
+        // a padded row reads the group's first row (32 w rows back)
+        const int64_t nr = static_cast<int>(32 * w + n) < rv ? static_cast<int64_t>(n) : -32LL * w;
+        const uint8_t* src = u < 64 ? qa + nr * (2 * kDc) + 16 * u : qr + nr * (2 * kDr) + 16 * (u - 64);
         lds_dma16_va(src, reg + 1024 * i);
       }
     };
@@ -1302,26 +1308,35 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
             static_cast<uintptr_t>(erd + 2 * s2 * kEpiRow));
       const int64_t row0 = rowg + 32 * (kF8M ? qq : w);
       const int col0 = 128 * (kF8M ? w : qq);
-      if (p.part_bf16) {
-        uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + col0;
+      // rows 2 s2 + li / 32 of the block exist below `lim` (all of them but
+      // in a padded group)
+      const int lim = rv - 32 * (kF8M ? qq : w) - static_cast<int>(li >> 5);
+      auto store_rows = [&](auto pred) {
+        if (p.part_bf16) {
+          uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + col0;
 #pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2) {
-          const bf16x2 lo = {static_cast<__bf16>(ev[s2][0]), static_cast<__bf16>(ev[s2][1])};
-          const bf16x2 hi = {static_cast<__bf16>(ev[s2][2]), static_cast<__bf16>(ev[s2][3])};
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          const u32x2 u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff));
+          for (int s2 = 0; s2 < 16; ++s2) {
+            const bf16x2 lo = {static_cast<__bf16>(ev[s2][0]), static_cast<__bf16>(ev[s2][1])};
+            const bf16x2 hi = {static_cast<__bf16>(ev[s2][2]), static_cast<__bf16>(ev[s2][3])};
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 u = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            if (!decltype(pred)::value || 2 * s2 < lim)
+              __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff));
+          }
+        } else {
+          float* ob = static_cast<float*>(o_part) + row0 * kDc + col0;
+#pragma unroll
+          for (int s2 = 0; s2 < 16; ++s2)
+            if (!decltype(pred)::value || 2 * s2 < lim)
+              __builtin_nontemporal_store(ev[s2], reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff));
         }
-      } else {
-        float* ob = static_cast<float*>(o_part) + row0 * kDc + col0;
-#pragma unroll
-        for (int s2 = 0; s2 < 16; ++s2)
-          __builtin_nontemporal_store(ev[s2], reinterpret_cast<f32x4*>(ob + 2 * s2 * kDc + eoff));
-      }
+      };
+      if (rv == kMfmaRows) store_rows(bool_c<false>{});
+      else store_rows(bool_c<true>{});
       __builtin_amdgcn_s_waitcnt(0xC07F);      // the reads are done before the next pass
       __builtin_amdgcn_wave_barrier();
     }
-    if ((li >> 5) == 0) {
+    if ((li >> 5) == 0 && w * 32 + static_cast<int>(li & 31) < rv) {
       const int64_t r = slot * p.rows + rg * kMfmaRows + w * 32 + static_cast<int>(li & 31);
       lse_part[r] = l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
       l_part[r] = l_row;
@@ -1342,7 +1357,7 @@ bool mfma_lds_plan(const mla_decode_desc* d) {
 bool mfma_supports(const mla_decode_desc* d) {
   return d->d_c == kDc && d->d_rope == kDr &&
          (d->cache_dtype == MLA_BF16 || d->cache_dtype == MLA_FP8_E4M3) &&
-         d->q_dtype == MLA_BF16 && (static_cast<int64_t>(d->q_len) * d->n_heads) % kMfmaRows == 0;
+         d->q_dtype == MLA_BF16;
 }
 
 mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {

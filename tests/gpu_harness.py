@@ -152,3 +152,27 @@ def assert_lse_close(g, r, tol: float, label: str = ""):
         say(f"  [{label}] lse max-abs {err:.3e}")
         assert err <= tol, (label, err)
     assert np.all(g[~fin] == -np.inf)
+
+
+def fp8_math_lse_tol(inp, batches=None, scale=None):
+    """Log-sum-exp gate of the fp8 matrix-core mode (MLA_DECODE_FP8_MATH):
+    2e-3 (the gate of the exact paths) plus the largest logit shift the
+    query rounding can cause. Rounding to e4m3
+    to nearest moves a normal value by at most 2^-4 of itself, and a
+    subnormal one (below 2^-6 after the block scaling, which puts the block
+    maximum at 128 or more) by at most 2^-10, i.e. 2^-17 of the block
+    maximum; so a content logit moves by at most
+    |scale| (2^-4 sum_k |q_k c_k| + 2^-17 max|q| sum_k |c_k|), and the
+    log-sum-exp by at most the largest of these."""
+    cfg = inp.cfg
+    sc = abs(cfg.softmax_scale if scale is None else scale)
+    qa, _ = oracle_queries(inp)
+    worst = 0.0
+    for b in (range(cfg.batch) if batches is None else batches):
+        c, _ = oracle_inputs(inp, b)
+        if len(c) == 0:
+            continue
+        q = np.abs(qa[b].reshape(-1, cfg.d_c))
+        bound = 2.0 ** -4 * (q @ np.abs(c).T) + 2.0 ** -17 * q.max() * np.abs(c).sum(1)[None, :]
+        worst = max(worst, float(bound.max()))
+    return 2e-3 + sc * worst

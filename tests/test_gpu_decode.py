@@ -265,3 +265,23 @@ def test_negative_and_zero_scale(base, factor):
     ro, rl = H.oracle_decode(inp, scale=scale)
     H.assert_close(o, ro, _kind(cfg), f"scale{factor:+g}-{base}")
     H.assert_lse_close(lse, rl, 2e-3, f"scale{factor:+g}-{base}")
+
+
+@pytest.mark.parametrize("n_h,q_len,dtype,flags", [
+    (16, 1, "bf16", 0), (32, 1, "bf16", 0), (8, 1, "bf16", 0), (48, 2, "bf16", 0),
+    (96, 2, "bf16", 0), (16, 2, "fp8", 0), (16, 1, "fp8", 1), (40, 3, "fp8", 1),
+])
+def test_row_counts_that_pad_the_last_row_group(n_h, q_len, dtype, flags):
+    """q_len x n_heads not a multiple of 128 (for example 16 local heads of a
+    head-sharded model): the matrix-core kernel pads the last 128-row group;
+    its missing rows load the group's first query row and are never stored.
+    96 x 2 = 192 rows gives one full group and one with 64 rows."""
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=3, n_heads=n_h, q_len=q_len, seq_len=None, ragged=(1, 300))
+    H.say(f"case padded rows n_h={n_h} q_len={q_len} rows={n_h * q_len} {dtype} flags={flags}")
+    inp = wl.make_decode_inputs(cfg, seq_lens=[q_len, 97, 700], q_mult=27.7)
+    o, lse = H.run_decode(inp, flags=flags)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, _kind(cfg), f"pad-n{n_h}-q{q_len}-{dtype}-{flags}")
+    tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
+    H.assert_lse_close(lse, rl, tol, f"pad-n{n_h}-q{q_len}-{dtype}-{flags}")

@@ -23,26 +23,7 @@ SMALL = wl.scaled(C["c5"], batch=4, seq_len=1000)
 
 
 def _lse_tol(inp, batches=None, scale=None):
-    """Log-sum-exp gate of this mode: 2e-3 (the gate of the exact paths) plus
-    the largest logit shift the query rounding can cause. Rounding to e4m3
-    to nearest moves a normal value by at most 2^-4 of itself, and a
-    subnormal one (below 2^-6 after the block scaling, which puts the block
-    maximum at 128 or more) by at most 2^-10, i.e. 2^-17 of the block
-    maximum; so a content logit moves by at most
-    |scale| (2^-4 sum_k |q_k c_k| + 2^-17 max|q| sum_k |c_k|), and the
-    log-sum-exp by at most the largest of these."""
-    cfg = inp.cfg
-    sc = abs(cfg.softmax_scale if scale is None else scale)
-    qa, _ = H.oracle_queries(inp)
-    worst = 0.0
-    for b in (range(cfg.batch) if batches is None else batches):
-        c, _ = H.oracle_inputs(inp, b)
-        if len(c) == 0:
-            continue
-        q = np.abs(qa[b].reshape(-1, cfg.d_c))
-        bound = 2.0 ** -4 * (q @ np.abs(c).T) + 2.0 ** -17 * q.max() * np.abs(c).sum(1)[None, :]
-        worst = max(worst, float(bound.max()))
-    return 2e-3 + sc * worst
+    return H.fp8_math_lse_tol(inp, batches, scale)
 
 
 def _check(inp, o, lse, label, batches=None, scale=None):
