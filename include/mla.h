@@ -79,8 +79,8 @@ typedef struct mla_decode_desc {
   int32_t flags;              /* 0, or MLA_DECODE_FP8_MATH */
 } mla_decode_desc;
 
-/* flags bit: with an FP8_E4M3 cache, d_c = 512, d_rope = 64, bf16 queries and
- * q_len * n_heads a multiple of 128, compute the content scores on the fp8
+/* flags bit: with an FP8_E4M3 cache, d_c = 512, d_rope = 64 and bf16 queries
+ * (the shapes the matrix-core kernel serves), compute the content scores on the fp8
  * matrix cores: the cached e4m3 codes are multiplied as stored against the
  * queries rounded to e4m3 (round to nearest even) after scaling each block of
  * 32 consecutive q_abs lanes by a power of two that puts its largest
