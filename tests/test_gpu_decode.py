@@ -285,3 +285,36 @@ def test_row_counts_that_pad_the_last_row_group(n_h, q_len, dtype, flags):
     H.assert_close(o, ro, _kind(cfg), f"pad-n{n_h}-q{q_len}-{dtype}-{flags}")
     tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
     H.assert_lse_close(lse, rl, tol, f"pad-n{n_h}-q{q_len}-{dtype}-{flags}")
+
+
+@pytest.mark.parametrize("dtype,flags", [("bf16", 0), ("fp8", 0), ("fp8", 1)])
+def test_pages_beyond_four_gib(dtype, flags):
+    """Page ids whose byte offsets exceed 2^32: the sequences' pages sit at
+    the top of a pool of a little over 4 GiB (the rest of the pool is never
+    read), so every cache address needs 64-bit arithmetic."""
+    import torch
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=2, seq_len=300)
+    H.say(f"case pages beyond 4 GiB {dtype} flags={flags}")
+    inp = wl.make_decode_inputs(cfg)
+    dev = H.device_inputs(inp)
+    pool = dev["cache"]
+    page_bytes = pool[0].numel() * pool.element_size()
+    first = (1 << 32) // page_bytes + 7          # first page id used
+    big = torch.empty((first + pool.shape[0],) + tuple(pool.shape[1:]), dtype=pool.dtype,
+                      device="cuda")
+    big[first:] = pool
+    assert first * page_bytes > (1 << 32)
+    dev["cache"] = big
+    if dev["cache_scale"] is not None:
+        sbig = torch.empty((first + pool.shape[0], 64), dtype=torch.float32, device="cuda")
+        sbig[first:] = dev["cache_scale"]
+        dev["cache_scale"] = sbig
+    bt = dev["block_table"]
+    dev["block_table"] = torch.where(bt >= 0, bt + first, bt)
+    dev["n_pages"] = first + pool.shape[0]
+    o, lse = H.run_decode(inp, dev=dev, flags=flags)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, _kind(cfg), f"4GiB-{dtype}-{flags}")
+    tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
+    H.assert_lse_close(lse, rl, tol, f"4GiB-{dtype}-{flags}")
