@@ -318,3 +318,49 @@ def test_pages_beyond_four_gib(dtype, flags):
     H.assert_close(o, ro, _kind(cfg), f"4GiB-{dtype}-{flags}")
     tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
     H.assert_lse_close(lse, rl, tol, f"4GiB-{dtype}-{flags}")
+
+
+@pytest.mark.parametrize("dtype,flags", [("bf16", 0), ("fp8", 1)])
+def test_graph_capture_replays_match_eager(dtype, flags):
+    """mla_decode issues kernels only (no allocation, no memset, no host
+    synchronisation), so it can be captured in a HIP graph: the graph is
+    replayed with new queries written into the captured buffers, with eager
+    work between replays, and every replay matches an eager call bitwise."""
+    import torch
+    m = H.lib()
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=3, seq_len=900)
+    H.say(f"case graph capture {dtype} flags={flags}")
+    inp = wl.make_decode_inputs(cfg)
+    dev = H.device_inputs(inp)
+    desc = m.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
+                         cfg.cache_dtype, "bf16", cfg.out_dtype, flags=flags)
+    ws = torch.empty(m.mla_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    qa, qr = dev["q_abs"].clone(), dev["q_rope"].clone()
+    shape = (cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c)
+    o_g = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    l_g = torch.empty(shape[:3], dtype=torch.float32, device="cuda")
+
+    def call(q1, q2, o, lse):
+        m.mla_decode(desc, q1, q2, dev["cache"], dev["cache_scale"], dev["block_table"],
+                     dev["seq_lens"], cfg.softmax_scale, o, lse, ws)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call(qa, qr, o_g, l_g)   # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(qa, qr, o_g, l_g)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(3):
+        qa.copy_((torch.randn(qa.shape, device="cuda", generator=gen) * 0.05).to(qa.dtype))
+        qr.copy_((torch.randn(qr.shape, device="cuda", generator=gen) * 0.05).to(qr.dtype))
+        o_e = torch.empty_like(o_g)
+        l_e = torch.empty_like(l_g)
+        call(qa, qr, o_e, l_e)   # eager reference (and eager work between replays)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), f"replay {rep}"
