@@ -364,3 +364,30 @@ def test_graph_capture_replays_match_eager(dtype, flags):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), f"replay {rep}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_sweep(seed):
+    """Seeded random shapes on the matrix-core path: batch, ragged lengths,
+    head count (any, so row groups pad), query tokens, cache dtype, fp8 flag,
+    split count and output dtype, each against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["bf16", "fp8"][int(rng.integers(0, 2))]
+    flags = int(rng.integers(0, 2)) if dtype == "fp8" else 0
+    n_h = int(rng.choice([1, 3, 8, 16, 24, 40, 64, 100, 128]))
+    q_len = int(rng.integers(1, 5))
+    batch = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(q_len, 900, size=batch)]
+    parts = int(rng.choice([0, 1, 3, 11]))
+    out = ["bf16", "fp32"][int(rng.integers(0, 2))]
+    base = C["c2"] if dtype == "bf16" else C["c5"]
+    cfg = wl.scaled(base, batch=batch, n_heads=n_h, q_len=q_len, seq_len=None,
+                    ragged=(1, 900), out_dtype=out)
+    H.say(f"case sweep seed={seed} {dtype} flags={flags} n_h={n_h} q_len={q_len} "
+          f"lens={lens} parts={parts} out={out}")
+    inp = wl.make_decode_inputs(cfg, seq_lens=lens, q_mult=27.7)
+    o, lse = H.run_decode(inp, num_partitions=parts, flags=flags)
+    ro, rl = H.oracle_decode(inp)
+    H.assert_close(o, ro, _kind(cfg), f"sweep-{seed}")
+    tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
+    H.assert_lse_close(lse, rl, tol, f"sweep-{seed}")
