@@ -151,6 +151,7 @@ mla_status prepare(const mla_decode_desc* d, const void* q_abs, const void* q_ro
   a->l_part = p->path == Path::Mfma ? reinterpret_cast<float*>(ws + p->lsum_off) : nullptr;
   a->o_latent = nullptr;
   a->lse_out = nullptr;
+  a->skip_whole = false;
   return MLA_OK;
 }
 
@@ -179,6 +180,7 @@ mla_status mla_decode(const mla_decode_desc* d, const void* q_abs, const void* q
   if (!aligned16(o_latent)) return fail(MLA_ERR_MISALIGNED, "o_latent must be 16-byte aligned");
   a.o_latent = o_latent;
   a.lse_out = lse_out;
+  a.skip_whole = p.path == Path::Mfma;   // that kernel writes whole sequences' output
   hipStream_t st = static_cast<hipStream_t>(stream);
   s = run_partial(a, st);
   if (s != MLA_OK) return s;

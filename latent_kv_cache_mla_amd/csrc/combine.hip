@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       const float* __restrict__ l_part,
                                                       void* __restrict__ o_latent,
                                                       float* __restrict__ lse_out,
-                                                      int B, int rows, int d_c, int64_t G) {
+                                                      int B, int rows, int d_c, int64_t G,
+                                                      int skip_whole) {
   static_assert(kWR == 1 || kWR == 2 || kWR == 4, "waves per row");
   __shared__ float red[kWR > 1 ? 4 : 1][kWR > 1 ? 64 * 8 : 1];   // per wavefront of the block
   __shared__ float wms[4][2];                                     // (m_q, s_q) per wavefront
@@ -107,6 +108,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     glo = range_of_page_dev(s0, P, G);
     n = range_of_page_dev(s1 - 1, P, G) - glo + 1;
   }
+  // one range holds the whole sequence: the decode kernel wrote its output
+  // (all wavefronts of the row leave together)
+  if (skip_whole && n == 1) return;
   const bool may_be_empty = G > P;
   auto nonempty = [&](int64_t j) {
     return !may_be_empty || range_begin_dev(glo + j + 1, P, G) != range_begin_dev(glo + j, P, G);
@@ -259,13 +263,16 @@ void launch_combine_t(const DecodeArgs& a, const PT* op, hipStream_t st) {
   const dim3 block(256), grid(static_cast<unsigned>((pairs * wr + 3) / 4));
   if (wr == 4)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 4>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G,
+                       a.skip_whole ? 1 : 0);
   else if (wr == 2)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 2>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G,
+                       a.skip_whole ? 1 : 0);
   else
     hipLaunchKernelGGL((combine_kernel<PT, OT, 1>), grid, block, 0, st, a.page_start, op, a.lse_part,
-                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G);
+                       a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G,
+                       a.skip_whole ? 1 : 0);
 }
 
 mla_status launch_combine(const DecodeArgs& a, hipStream_t st) {

@@ -337,7 +337,8 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint8_t* __restrict__ cache, const float* __restrict__ cache_scale,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens,
     int32_t* __restrict__ page_start, void* __restrict__ o_part, float* __restrict__ lse_part,
-    float* __restrict__ l_part, MfmaParams p) {
+    float* __restrict__ l_part, void* __restrict__ o_out, float* __restrict__ lse_out,
+    MfmaParams p) {
   constexpr bool kFp8 = kMode == 1;   // fp8 cache, dequantised in LDS
   constexpr bool kF8M = kMode == 2;   // fp8 cache on the fp8 matrix cores
   // ring of chunk stages: chunk k lives in stage k % kS (fp8 dequantised: plus
@@ -353,6 +354,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
   __shared__ int ps_lds[kLdsPlan ? kMaxB + 1 : 1];   // page prefix sums
   __shared__ int lens_lds[kLdsPlan ? kMaxB : 1];     // clamped sequence lengths
   __shared__ int wtot_lds[4];                               // per-wave page totals
+  __shared__ float inv_lds[kMfmaRows];                      // 1 / row sum, whole-sequence pieces
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -481,6 +483,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const int64_t s0 = PS(b), s1 = PS(b + 1);
     if (s1 == s0) continue;
     const int64_t a0 = s0 > pb ? s0 : pb, a1 = s1 < pe ? s1 : pe;
+    // a piece that holds every page of its sequence writes the final output
+    // itself (normalised, in the output dtype, with its log-sum-exp) when the
+    // caller passed it; the combine then skips that sequence
+    const bool whole = o_out != nullptr && a0 == s0 && a1 == s1;
     const int n_pages = static_cast<int>(a1 - a0);
     int S;
     if constexpr (kLdsPlan) S = lens_lds[b];
@@ -1280,7 +1286,10 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
     const uint32_t erd = ewave + (li >> 5) * kEpiRow + (li & 31) * 16;   // row li / 32, unit li % 32
     // rows of pass qq: the wave's own 32 rows (columns 128 qq ..), or in the
     // fp8 matrix-core mode row block qq (the wave's columns 128 w ..)
-    const int64_t rowg = slot * p.rows + rg * kMfmaRows;
+    // (a whole-sequence piece: output rows b * rows + ..., each divided by its
+    // row sum, whose inverses the row owners publish in LDS first)
+    const int64_t rowg = (whole ? static_cast<int64_t>(b) : slot) * p.rows + rg * kMfmaRows;
+    if (whole && (li >> 5) == 0) inv_lds[w * 32 + (li & 31)] = l_row > 0.f ? 1.f / l_row : 0.f;
     __syncthreads();                           // every wave is done with the stages
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) {
@@ -1308,12 +1317,18 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
             static_cast<uintptr_t>(erd + 2 * s2 * kEpiRow));
       const int64_t row0 = rowg + 32 * (kF8M ? qq : w);
       const int col0 = 128 * (kF8M ? w : qq);
+      if (whole) {
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2)
+          ev[s2] *= inv_lds[32 * (kF8M ? qq : w) + 2 * s2 + static_cast<int>(li >> 5)];
+      }
+      void* const obase = whole ? o_out : o_part;
       // rows 2 s2 + li / 32 of the block exist below `lim` (all of them but
       // in a padded group)
       const int lim = rv - 32 * (kF8M ? qq : w) - static_cast<int>(li >> 5);
       auto store_rows = [&](auto pred) {
         if (p.part_bf16) {
-          uint16_t* ob = static_cast<uint16_t*>(o_part) + row0 * kDc + col0;
+          uint16_t* ob = static_cast<uint16_t*>(obase) + row0 * kDc + col0;
 #pragma unroll
           for (int s2 = 0; s2 < 16; ++s2) {
             const bf16x2 lo = {static_cast<__bf16>(ev[s2][0]), static_cast<__bf16>(ev[s2][1])};
@@ -1324,7 +1339,7 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
               __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(ob + 2 * s2 * kDc + eoff));
           }
         } else {
-          float* ob = static_cast<float*>(o_part) + row0 * kDc + col0;
+          float* ob = static_cast<float*>(obase) + row0 * kDc + col0;
 #pragma unroll
           for (int s2 = 0; s2 < 16; ++s2)
             if (!decltype(pred)::value || 2 * s2 < lim)
@@ -1337,9 +1352,14 @@ __global__ __launch_bounds__(256, 1) void decode_mfma_bf16(
       __builtin_amdgcn_wave_barrier();
     }
     if ((li >> 5) == 0 && w * 32 + static_cast<int>(li & 31) < rv) {
-      const int64_t r = slot * p.rows + rg * kMfmaRows + w * 32 + static_cast<int>(li & 31);
-      lse_part[r] = l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
-      l_part[r] = l_row;
+      const float lse = l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+      const int64_t r = rowg + w * 32 + static_cast<int>(li & 31);
+      if (whole) {
+        if (lse_out != nullptr) lse_out[r] = lse;
+      } else {
+        lse_part[r] = lse;
+        l_part[r] = l_row;
+      }
     }
   }
 }
@@ -1387,7 +1407,7 @@ mla_status launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<const uint16_t*>(a.q_abs),
                      static_cast<const uint16_t*>(a.q_rope), static_cast<const uint8_t*>(a.cache),
                      a.cache_scale, a.block_table, a.seq_lens, const_cast<int32_t*>(a.page_start),
-                     a.o_part, a.lse_part, a.l_part, p);
+                     a.o_part, a.lse_part, a.l_part, a.o_latent, a.lse_out, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode_mfma launch: %s", hipGetErrorString(e));
   return MLA_OK;

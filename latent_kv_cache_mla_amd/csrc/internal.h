@@ -57,8 +57,12 @@ struct DecodeArgs {
   // row sums of unnormalised partials (MFMA path); nullptr: the partials are
   // already normalised (generic path)
   float* l_part;
+  // final output; the matrix-core kernel writes the rows of every sequence
+  // that one piece covers whole straight here (nullptr: partials only)
   void* o_latent;
   float* lse_out;
+  // the combine skips sequences covered by one piece (their output is written)
+  bool skip_whole;
 };
 
 mla_status launch_decode_generic(const DecodeArgs& a, hipStream_t st);

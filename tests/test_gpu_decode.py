@@ -391,3 +391,46 @@ def test_random_shape_sweep(seed):
     H.assert_close(o, ro, _kind(cfg), f"sweep-{seed}")
     tol = 2e-3 if flags == 0 else H.fp8_math_lse_tol(inp)
     H.assert_lse_close(lse, rl, tol, f"sweep-{seed}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_partial_then_combine_matches_the_fused_call(dtype):
+    """mla_decode_partial followed by mla_decode_combine (partials for every
+    piece) against mla_decode (which writes the sequences that one piece
+    covers whole straight from its accumulators): both match the oracle, and
+    the sequences cut into several pieces agree bitwise."""
+    import torch
+    m = H.lib()
+    base = C["c2"] if dtype == "bf16" else wl.scaled(C["c5"], q_len=1)
+    cfg = wl.scaled(base, batch=4, seq_len=None, ragged=(1, 3000))
+    lens = [700, 64, 3000, 0]
+    H.say(f"case partial+combine {dtype} lens={lens}")
+    inp = wl.make_decode_inputs(cfg, seq_lens=lens, q_mult=27.7)
+    dev = H.device_inputs(inp)
+    o1, l1 = H.run_decode(inp, dev=dev, num_partitions=5)
+    desc = m.decode_desc(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"],
+                         cfg.cache_dtype, "bf16", cfg.out_dtype, 5)
+    ws = torch.empty(m.mla_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    o2 = torch.full((cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_c), float("nan"),
+                    dtype=torch.bfloat16, device="cuda")
+    l2 = torch.full((cfg.batch, cfg.q_len, cfg.n_heads), float("nan"), dtype=torch.float32,
+                    device="cuda")
+    m.mla_decode_partial(desc, dev["q_abs"], dev["q_rope"], dev["cache"], dev["cache_scale"],
+                         dev["block_table"], dev["seq_lens"], cfg.softmax_scale, ws)
+    m.mla_decode_combine(desc, ws, o2, l2)
+    torch.cuda.synchronize()
+    o2 = o2.float().cpu().numpy().astype(np.float64)
+    l2 = l2.cpu().numpy().astype(np.float64)
+    ro, rl = H.oracle_decode(inp)
+    for o, l, tag in ((o1, l1, "fused"), (o2, l2, "split")):
+        H.assert_close(o, ro, _kind(cfg), f"{tag}-{dtype}")
+        H.assert_lse_close(l, rl, 2e-3, f"{tag}-{dtype}")
+    # pages 11, 1, 47, 0 in 5 ranges starting at pages 0, 11, 23, 35, 47:
+    # sequences 0 and 1 lie inside one range each (written directly by the
+    # fused call, without the bf16 partial rounding of the split path),
+    # sequence 2 crosses four ranges, sequence 3 is empty
+    assert np.array_equal(o1[2], o2[2]) and np.array_equal(l1[2], l2[2])
+    for b in (0, 1):
+        assert np.max(np.abs(o1[b] - o2[b])) < 1e-3, b
+    assert np.all(o1[3] == 0) and np.all(o2[3] == 0) and np.all(np.isneginf(l1[3]))
