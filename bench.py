@@ -104,6 +104,42 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"fp64 numpy oracle, {t_total:.1f} s of CPU time"}
 
 
+def measured_read_gbs(n_bytes: int = 1 << 30, reps: int = 10):
+    """Achievable HBM read bandwidth: row sums over n_bytes of fp32 in rows of
+    1024 (the fastest plain reduction shape measured here; the output is 1/1024
+    of the input), untimed warm-up, then the best of `reps` timed passes."""
+    import torch
+    x = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda").view(-1, 1024)
+    out = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        torch.sum(x, dim=1, out=out)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.sum(x, dim=1, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del x
+    return round(n_bytes / best / 1e9, 1)
+
+
+def gpu_clocks():
+    """Current shader and memory clocks as rocm-smi reports them (None if it
+    cannot be run)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+        card = d[sorted(d)[0]]
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    except Exception:   # no rocm-smi, no permission, unexpected output
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +284,10 @@ def main():
                                  "frac": round(k_tfs / BF16_MFMA_PEAK_TFS, 4),
                                  "algorithmic_flops_per_launch": flops,
                                  "hbm_achieved_gbs": round(k_gbs, 2)})
+    # context for the roofline: a measured streaming read (a plain reduction
+    # over 1 GiB, far larger than the 256 MB last-level cache) and the clocks
+    line["hbm_read_measured_gbs"] = measured_read_gbs()
+    line["clocks"] = gpu_clocks()
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
