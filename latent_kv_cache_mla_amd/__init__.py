@@ -113,6 +113,42 @@ def _dev(t, name):
     return t
 
 
+class MlaArgumentError(MlaError):
+    """A buffer too small for what the descriptor says the call touches,
+    found by the binding before the C call (no device access happened)."""
+
+    def __init__(self, where: str, msg: str):
+        self.status = MLA_ERR_INVALID_ARGUMENT
+        RuntimeError.__init__(self, f"{where}: MLA_ERR_INVALID_ARGUMENT: {msg}")
+
+
+_ELEM = {MLA_FP32: 4, MLA_BF16: 2}
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _need(t, nbytes, name, where):
+    """`t` must hold at least `nbytes` bytes (a size check only: the library
+    reads or writes exactly that many through the pointer)."""
+    if t is not None and _nbytes(t) < nbytes:
+        raise MlaArgumentError(where, f"{name} holds {_nbytes(t)} bytes, the descriptor needs {nbytes}")
+
+
+def _check_decode_buffers(desc, where, q_abs=None, q_rope=None, block_table=None, seq_lens=None,
+                          o_latent=None, lse_out=None):
+    rows = int(desc.batch) * int(desc.q_len) * int(desc.n_heads)
+    qe = _ELEM.get(int(desc.q_dtype), 4)
+    oe = _ELEM.get(int(desc.out_dtype), 4)
+    _need(q_abs, rows * int(desc.d_c) * qe, "q_abs", where)
+    _need(q_rope, rows * int(desc.d_rope) * qe, "q_rope", where)
+    _need(block_table, int(desc.batch) * int(desc.max_blocks_per_seq) * 4, "block_table", where)
+    _need(seq_lens, int(desc.batch) * 4, "seq_lens", where)
+    _need(o_latent, rows * int(desc.d_c) * oe, "o_latent", where)
+    _need(lse_out, rows * 4, "lse_out", where)
+
+
 def decode_desc(batch, q_len, n_heads, d_c, d_rope, max_blocks_per_seq, cache_dtype="bf16",
                 q_dtype="bf16", out_dtype="bf16", num_partitions=0, plan_ready=0,
                 flags=0) -> MlaDecodeDesc:
@@ -134,6 +170,7 @@ def mla_decode_workspace_size(desc: MlaDecodeDesc) -> int:
 
 
 def mla_decode_plan(desc, seq_lens, workspace, stream=None):
+    _check_decode_buffers(desc, "mla_decode_plan", seq_lens=seq_lens)
     _check(lib.mla_decode_plan(ctypes.byref(desc), _ptr(_dev(seq_lens, "seq_lens")),
                                _ptr(_dev(workspace, "workspace")), workspace.numel() * workspace.element_size(),
                                _stream(stream)), "mla_decode_plan")
@@ -145,6 +182,8 @@ def mla_decode(desc, q_abs, q_rope, cache, cache_scale, block_table, seq_lens, s
                  (block_table, "block_table"), (seq_lens, "seq_lens"), (o_latent, "o_latent"),
                  (lse_out, "lse_out"), (workspace, "workspace")):
         _dev(t, n)
+    _check_decode_buffers(desc, "mla_decode", q_abs, q_rope, block_table, seq_lens, o_latent,
+                          lse_out)
     _check(lib.mla_decode(ctypes.byref(desc), _ptr(q_abs), _ptr(q_rope), _ptr(cache),
                           _ptr(cache_scale), _ptr(block_table), _ptr(seq_lens), float(scale),
                           _ptr(o_latent), _ptr(lse_out), _ptr(workspace),
@@ -157,6 +196,7 @@ def mla_decode_partial(desc, q_abs, q_rope, cache, cache_scale, block_table, seq
     for t, n in ((q_abs, "q_abs"), (q_rope, "q_rope"), (cache, "cache"), (cache_scale, "cache_scale"),
                  (block_table, "block_table"), (seq_lens, "seq_lens"), (workspace, "workspace")):
         _dev(t, n)
+    _check_decode_buffers(desc, "mla_decode_partial", q_abs, q_rope, block_table, seq_lens)
     _check(lib.mla_decode_partial(ctypes.byref(desc), _ptr(q_abs), _ptr(q_rope), _ptr(cache),
                                   _ptr(cache_scale), _ptr(block_table), _ptr(seq_lens),
                                   float(scale), _ptr(workspace),
@@ -165,6 +205,7 @@ def mla_decode_partial(desc, q_abs, q_rope, cache, cache_scale, block_table, seq
 
 
 def mla_decode_combine(desc, workspace, o_latent, lse_out=None, stream=None):
+    _check_decode_buffers(desc, "mla_decode_combine", o_latent=o_latent, lse_out=lse_out)
     _check(lib.mla_decode_combine(ctypes.byref(desc), _ptr(_dev(workspace, "workspace")),
                                   workspace.numel() * workspace.element_size(),
                                   _ptr(_dev(o_latent, "o_latent")), _ptr(_dev(lse_out, "lse_out")),

@@ -36,8 +36,8 @@ identities and closed forms. The RoPE pair layout and rotation direction are
 a free choice (any fixed choice preserves the relative-position property).
 """
 from .reference import (  # noqa: F401
-    rope, softmax, mla_unabsorbed, mla_absorbed, latent_attention,
-    decode_batch, fold_query, fold_output, output_projection_merged,
+    rope, softmax, score_scale, mla_unabsorbed, mla_absorbed, latent_attention,
+    fold_query, fold_output, output_projection_merged,
     output_projection_two_stage, cache_append, absorb_query,
 )
 from .formats import (  # noqa: F401

@@ -75,6 +75,14 @@ def _head(W, i, width):
     return W[i * width:(i + 1) * width]
 
 
+def score_scale(d_h: int, d_rope: int) -> float:
+    """The factor applied to a summed content + rope score: one over the
+    square root of one head's content width plus its rope width ([Zhang]
+    "Value absorption: weight and sum first, project after": 128 + 64 for
+    DeepSeek-V2). The latent width d_c does not enter it."""
+    return 1.0 / math.sqrt(d_h + d_rope)
+
+
 # ----------------------------------------------------------------------------
 # O1: the unabsorbed definition
 # ----------------------------------------------------------------------------
@@ -97,7 +105,7 @@ def mla_unabsorbed(model, q_len: int = 1, pos0: int = 0) -> dict:
     pos = pos0 + np.arange(S)
     W = {k: None if v is None else np.asarray(v, dtype=np.float64)
          for k, v in model.__dict__.items() if k.startswith("W_")}
-    scale = 1.0 / math.sqrt(dh + dr)
+    scale = score_scale(dh, dr)
 
     c = H @ W["W_DKV"].T                                     # [S, d_c]
     kR = rope(H @ W["W_KR"].T, pos, cfg.rope_theta)          # [S, d_R]
@@ -201,20 +209,6 @@ def latent_attention(q_abs, q_rope, c, kR, scale: float) -> dict:
     return dict(o=o, lse=_log_sum_exp(s), scores=s, attn=a)
 
 
-def decode_batch(q_abs, q_rope, latents, krope, scale: float) -> tuple[np.ndarray, np.ndarray]:
-    """A batch of sequences: q_abs [B, q_len, n_h, d_c], q_rope
-    [B, q_len, n_h, d_R], latents/krope lists of per-sequence [S_b, .] arrays
-    (fp64 values as stored). Returns (o [B, q_len, n_h, d_c], lse
-    [B, q_len, n_h])."""
-    B, q_len, nh, dc = np.shape(q_abs)
-    o = np.zeros((B, q_len, nh, dc))
-    lse = np.zeros((B, q_len, nh))
-    for b in range(B):
-        r = latent_attention(q_abs[b], q_rope[b], latents[b], krope[b], scale)
-        o[b], lse[b] = r["o"], r["lse"]
-    return o, lse
-
-
 # ----------------------------------------------------------------------------
 # O2: the absorbed CPU form
 # ----------------------------------------------------------------------------
@@ -255,7 +249,7 @@ def mla_absorbed(model, q_len: int = 1, pos0: int = 0) -> dict:
     H = model.H.astype(np.float64)
     S = H.shape[0]
     pos = pos0 + np.arange(S)
-    scale = 1.0 / math.sqrt(dh + dr)
+    scale = score_scale(dh, dr)
     W_qabs = fold_query(model.W_UQ, model.W_UK, nh, dh)
     W_ov = fold_output(model.W_O, model.W_UV, nh, dh)
     c, kR = cache_append(model.W_DKV, model.W_KR, H, pos, cfg.rope_theta)

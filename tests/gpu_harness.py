@@ -28,33 +28,7 @@ def lib():
     return m
 
 
-def to_dev(a: np.ndarray, dtype=None) -> torch.Tensor:
-    t = torch.from_numpy(np.ascontiguousarray(a))
-    if dtype is not None:
-        t = t.view(dtype)
-    return t.cuda()
-
-
-def device_inputs(inp: wl.DecodeInputs, max_blocks: int | None = None):
-    """Device tensors for one decode call (paged cache, table, lengths, queries)."""
-    cfg = inp.cfg
-    pool, spool = wl.paged_cache(inp)
-    bt = wl.block_table(inp.seq_lens, inp.page_perm, max_blocks)
-    dev = {
-        "cache": to_dev(pool),
-        "cache_scale": None if spool is None else to_dev(spool.astype(np.float32)),
-        "block_table": to_dev(bt),
-        "seq_lens": to_dev(inp.seq_lens.astype(np.int32)),
-        "n_pages": pool.shape[0],
-        "max_blocks": bt.shape[1],
-    }
-    if cfg.cache_dtype == "fp32":
-        dev["q_abs"] = to_dev(inp.q_abs_f32)
-        dev["q_rope"] = to_dev(inp.q_rope_f32)
-    else:
-        dev["q_abs"] = to_dev(inp.q_abs_bits.view(np.int16)).view(torch.bfloat16)
-        dev["q_rope"] = to_dev(inp.q_rope_bits.view(np.int16)).view(torch.bfloat16)
-    return dev
+from workloads.device import device_inputs, to_dev  # noqa: E402,F401
 
 
 def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: bool = True,
@@ -176,3 +150,35 @@ def fp8_math_lse_tol(inp, batches=None, scale=None):
         bound = 2.0 ** -4 * (q @ np.abs(c).T) + 2.0 ** -17 * q.max() * np.abs(c).sum(1)[None, :]
         worst = max(worst, float(bound.max()))
     return 2e-3 + sc * worst
+
+
+def stress_inputs(cfg, variant: str, needle_seed: int = 77):
+    """Seeded inputs whose attention is far from uniform (the gated workloads'
+    logits have a standard deviation near 0.003):
+      sharp        queries x 27.7 (logit standard deviation about 2);
+      rope_only    sharp, with the content queries zero;
+      content_only sharp, with the rope queries zero;
+      needle       rope query e_0 for every head and one token per sequence
+                   whose rope key is (20 / scale) e_0: a +20 logit that takes
+                   almost all of the weight (the other queries stay sharp)."""
+    inp = wl.make_decode_inputs(cfg, q_mult=27.7)
+    if variant == "rope_only":
+        inp.q_abs_bits[...] = 0
+    elif variant == "content_only":
+        inp.q_rope_bits[...] = 0
+    elif variant == "needle":
+        inp.q_rope_bits[...] = 0
+        inp.q_rope_bits[..., 0] = wl.to_bf16_bits(np.array([1.0]))[0]
+        rng = np.random.default_rng(needle_seed)
+        val = wl.to_bf16_bits(np.array([20.0 / cfg.softmax_scale]))[0]
+        for b in range(cfg.batch):
+            S = int(inp.seq_lens[b])
+            if S < cfg.q_len:
+                continue
+            j = int(rng.integers(0, S - cfg.q_len + 1))
+            kr = inp.krope_bits[b] if cfg.cache_dtype == "fp8" else inp.lat_bits[b][:, cfg.d_c:]
+            kr[j, :] = 0
+            kr[j, 0] = val
+    elif variant != "sharp":
+        raise ValueError(variant)
+    return inp

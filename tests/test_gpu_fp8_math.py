@@ -41,15 +41,16 @@ def test_reduced_speculative_pair():
     _check(inp, o, lse, "f8m-c5-reduced")
 
 
-def test_full_size_sampled():
-    """The full c5 shape in the launch configuration the benchmark times; the
-    oracle checks 16 sampled sequences (both query tokens, all heads)."""
+@pytest.mark.parametrize("variant", ["workload", "sharp", "needle"])
+def test_full_size(variant):
+    """The full c5 shape in the launch configuration the benchmark times, on
+    the workload's own inputs and with sharp or needle attention; every
+    sequence, both query tokens, all heads and lanes."""
     cfg = C["c5"]
-    H.say(f"case fp8-math c5-full B={cfg.batch} q_len={cfg.q_len}")
-    inp = wl.make_decode_inputs(cfg)
+    H.say(f"case fp8-math c5-full-{variant} B={cfg.batch} q_len={cfg.q_len}")
+    inp = wl.make_decode_inputs(cfg) if variant == "workload" else H.stress_inputs(cfg, variant)
     o, lse = H.run_decode(inp, flags=F8)
-    bs = sorted(np.random.default_rng(56).choice(cfg.batch, 16, replace=False).tolist())
-    _check(inp, o[bs], lse[bs], "f8m-c5-full-sampled", bs)
+    _check(inp, o, lse, f"f8m-c5-full-{variant}")
 
 
 def test_close_to_the_dequantising_path():

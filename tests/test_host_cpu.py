@@ -143,3 +143,74 @@ def test_partition_arithmetic_under_sanitizers(tmp_path):
                     "-fno-sanitize-recover=all", src, "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+# ----------------------------------------------------------------------------
+# build guards of the matrix-core kernel
+# ----------------------------------------------------------------------------
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _have_hipcc():
+    return os.path.exists(HIPCC)
+
+
+@pytest.mark.skipif(not _have_hipcc(), reason="hipcc not installed")
+def test_decode_kernels_use_no_scratch(tmp_path):
+    """Every instantiation of the matrix-core decode kernel compiles with no
+    scratch memory and no vector-register spills (its speed depends on that:
+    a scratch reload waits for every memory operation in flight, including
+    the cache copies), one wavefront per SIMD, and LDS within 160 KB."""
+    src = os.path.join(ROOT, "latent_kv_cache_mla_amd", "csrc", "decode_mfma.hip")
+    r = subprocess.run([HIPCC, *DEVICE_FLAGS, "-c", src, "-o", str(tmp_path / "d.o"),
+                        "-Rpass-analysis=kernel-resource-usage"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    blocks = re.split(r"remark: Function Name: ", r.stderr)[1:]
+    kernels = {}
+    for blk in blocks:
+        name = blk.split()[0]
+        field = lambda k: int(re.search(rf"{k}: (\d+)", blk).group(1))  # noqa: E731
+        kernels[name] = {"scratch": field(r"ScratchSize \[bytes/lane\]"),
+                         "vspill": field("VGPRs Spill"), "lds": field(r"LDS Size \[bytes/block\]")}
+    decode = {k: v for k, v in kernels.items() if "decode_mfma" in k}
+    assert len(decode) >= 6, sorted(kernels)
+    for name, v in decode.items():
+        assert v["scratch"] == 0 and v["vspill"] == 0, (name, v)
+        assert v["lds"] <= 160 * 1024, (name, v)
+
+
+@pytest.mark.skipif(not _have_hipcc(), reason="hipcc not installed")
+def test_wait_states_after_inline_matrix_ops_cover_the_hazard(tmp_path):
+    """The score MFMAs are inline asm, which the compiler's hazard checker does
+    not see into; the last of each chain is followed by 16 wait states
+    (s_nop 7, twice) before vector-ALU code reads its result. Ask the compiler
+    how many it places itself between the same instruction and a dependent
+    vector-ALU read, and check that 16 covers it."""
+    src = tmp_path / "probe.hip"
+    src.write_text(
+        "#include <hip/hip_runtime.h>\n"
+        "typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));\n"
+        "typedef float f32x16 __attribute__((ext_vector_type(16)));\n"
+        "__global__ void probe(float* out, const bf16x8* a, const bf16x8* b) {\n"
+        "  const int t = threadIdx.x;\n"
+        "  f32x16 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], b[t], f32x16{}, 0, 0, 0);\n"
+        "  out[t] = c[0] * 3.0f + c[5];\n"
+        "}\n")
+    asm = tmp_path / "probe.s"
+    r = subprocess.run([HIPCC, *DEVICE_FLAGS, "-S", str(src), "-o", str(asm)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = asm.read_text().splitlines()
+    i = next(k for k, l in enumerate(lines) if "v_mfma_f32_32x32x16_bf16" in l)
+    needed = 0
+    for l in lines[i + 1:]:
+        m = re.match(r"\s*s_nop\s+(\d+)", l)
+        if not m:
+            break
+        needed += int(m.group(1)) + 1
+    assert 0 < needed <= 16, needed
+    kernel = open(os.path.join(ROOT, "latent_kv_cache_mla_amd", "csrc", "decode_mfma.hip")).read()
+    assert 'v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\\n\\ts_nop 7\\n\\ts_nop 7' in kernel

@@ -1,6 +1,7 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch each one: a dropped rope term, a wrong softmax scale, an off-by-one
-causal limit, a wrong head index in the fold, a wrong RoPE frequency."""
+causal limit, a wrong head index in the fold, a wrong RoPE frequency, and a
+wrong scale shared by the unabsorbed and the absorbed forms."""
 import math
 
 import numpy as np
@@ -68,3 +69,28 @@ def test_planted_rope_frequency_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "rope", bad_rope)
     with pytest.raises(AssertionError):
         pins.test_rope_equals_complex_rotation()
+
+
+@pytest.mark.parametrize("wrong", ["d_h", "latent_width"])
+def test_planted_common_scale_is_caught(monkeypatch, wrong):
+    """The same wrong scale in O1 and O2 (1/sqrt(d_h), as one of the pages
+    writes for plain attention, or 1/sqrt(d_c + d_R)): the absorbed/unabsorbed
+    identity cannot see it, the page's denominator and the brute-force scores
+    must."""
+    def bad_scale(d_h, d_rope):
+        return 1.0 / math.sqrt(d_h if wrong == "d_h" else 512 + d_rope)
+    monkeypatch.setattr(ref, "score_scale", bad_scale)
+    monkeypatch.setattr(oracle, "score_scale", bad_scale)
+    golden = pins_golden()
+    pins.test_tiny_config_absorbed_equals_unabsorbed()   # common mode: still agrees
+    with pytest.raises(AssertionError):
+        pins.test_score_scale_is_the_pages_denominator(golden)
+    with pytest.raises(AssertionError):
+        pins.test_unabsorbed_scores_brute_force(golden)
+
+
+def pins_golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")) as f:
+        return json.load(f)

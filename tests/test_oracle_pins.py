@@ -333,3 +333,67 @@ def test_bf16_decode_matches_torch():
     bits = bits[(bits & 0x7F80) != 0x7F80]          # finite only
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(oracle.bf16_bits_to_f64(bits), ref)
+
+
+# ----------------------------------------------------------------------------
+# the softmax scale: the page fixes the denominator
+# ----------------------------------------------------------------------------
+
+def test_score_scale_is_the_pages_denominator(golden):
+    """[Zhang] "Value absorption": the summed content and rope score is divided
+    by the square root of 128 + 64 for the DeepSeek head; the same rule gives
+    64 + 16 for the tiny model's heads. Not sqrt(d_h), not sqrt(576)."""
+    g = golden["score_scale_denominator_squared"]
+    assert g["d_h"] + g["d_R"] == g["value"]
+    assert oracle.score_scale(g["d_h"], g["d_R"]) == 1.0 / math.sqrt(g["value"])
+    assert oracle.score_scale(64, 16) == 1.0 / math.sqrt(80)
+    for wrong in (1.0 / math.sqrt(g["d_h"]), 1.0 / math.sqrt(512 + g["d_R"])):
+        assert oracle.score_scale(g["d_h"], g["d_R"]) != wrong
+
+
+def _py_matvec(W, x):
+    return [sum(W[r][k] * x[k] for k in range(len(x))) for r in range(len(W))]
+
+
+def _py_rope(x, pos, theta):
+    """Rotation of interleaved pairs (2k, 2k+1) by pos * theta^(-2k/d), one
+    pair at a time (the oracle's layout reading, written out)."""
+    d = len(x)
+    out = list(x)
+    for k in range(d // 2):
+        ang = pos * theta ** (-2.0 * k / d)
+        cs, sn = math.cos(ang), math.sin(ang)
+        out[2 * k] = x[2 * k] * cs - x[2 * k + 1] * sn
+        out[2 * k + 1] = x[2 * k] * sn + x[2 * k + 1] * cs
+    return out
+
+
+def test_unabsorbed_scores_brute_force(golden):
+    """O1's scores at the DeepSeek head widths (d_h 128, d_R 64; two heads,
+    tiny d_c and d_model) recomputed in plain Python loops from the weights:
+    q_i = [W^UQ_i h_t ; RoPE(W^QR_i h_t)], k_{j,i} = [W^UK_i W^DKV h_j ;
+    RoPE(W^KR h_j)], score = (q_i . k_{j,i}) / sqrt(192) with 192 the page's
+    128 + 64 ([Mishra] "Step 4: decoupled RoPE"; [Zhang] "Value absorption").
+    Independent of the absorbed form O2, so a wrong scale shared by O1 and O2
+    fails here."""
+    g = golden["score_scale_denominator_squared"]
+    dh, dr = g["d_h"], g["d_R"]
+    cfg = wl.scaled(wl.CONFIGS["tiny"], n_heads=2, d_head=dh, d_rope=dr, d_c=8, d_model=6,
+                    seq_len=3)
+    model = wl.make_tiny_model(cfg, seed=21)
+    r = oracle.mla_unabsorbed(model)
+    W = {k: np.asarray(v, np.float64).tolist() for k, v in model.__dict__.items()
+         if k.startswith("W_") and v is not None}
+    H = np.asarray(model.H, np.float64).tolist()
+    S, t = len(H), len(H) - 1
+    theta = cfg.rope_theta
+    c = [_py_matvec(W["W_DKV"], H[j]) for j in range(S)]
+    kR = [_py_rope(_py_matvec(W["W_KR"], H[j]), j, theta) for j in range(S)]
+    for i in range(cfg.n_heads):
+        qC = _py_matvec(W["W_UQ"][i * dh:(i + 1) * dh], H[t])
+        qR = _py_rope(_py_matvec(W["W_QR"][i * dr:(i + 1) * dr], H[t]), t, theta)
+        for j in range(S):
+            kC = _py_matvec(W["W_UK"][i * dh:(i + 1) * dh], c[j])
+            dot = sum(a * b for a, b in zip(qC + qR, kC + kR[j]))
+            want = dot / math.sqrt(g["value"])
+            assert abs(r["scores"][0, i, j] - want) <= 1e-12 * max(1.0, abs(want)), (i, j)

@@ -1,4 +1,6 @@
 """The seeded input generators: storage conversions and layout (CPU)."""
+import math
+
 import numpy as np
 import torch
 
@@ -64,3 +66,80 @@ def test_draws_are_reproducible():
     a, b = wl.make_decode_inputs(cfg), wl.make_decode_inputs(cfg)
     assert np.array_equal(a.q_abs_bits, b.q_abs_bits)
     assert all(np.array_equal(x, y) for x, y in zip(a.lat_bits, b.lat_bits))
+
+
+# ----------------------------------------------------------------------------
+# the configurations against the workload text they were transcribed from
+# ----------------------------------------------------------------------------
+
+def _spec():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "workload_spec.json")
+    with open(path) as f:
+        return json.load(f)["workloads"]
+
+
+def _parse(text: str, inherit: dict) -> dict:
+    """Numbers of one workload description; fields a description leaves to
+    another ("same 128-head bf16 shapes") come from `inherit`."""
+    import re
+
+    def num(pat):
+        m = re.search(pat, text)
+        return int(m.group(1)) if m else None
+    f = dict(inherit)
+    for key, pat in (("batch", r"[Bb]atch (\d+)"), ("seq_len", r"context (\d+)"),
+                     ("n_heads", r"n_h=(\d+)"), ("d_c", r"d_c=(\d+)"), ("d_rope", r"d_R=(\d+)"),
+                     ("d_head", r"d_h=(\d+)"), ("d_model", r"d_model=(\d+)"),
+                     ("scale_sq", r"1/sqrt\((\d+)\)")):
+        v = num(pat)
+        if v is not None:
+            f[key] = v
+    v = num(r"(\d+)-head") or num(r"(\d+) heads")
+    if v is not None:
+        f["n_heads"] = v
+    v = num(r"(\d+) query tokens?")
+    if v is not None:
+        f["q_len"] = v
+    m = re.search(r"uniform in \[(\d+), (\d+)\]", text)
+    f["ragged"] = (int(m.group(1)), int(m.group(2))) if m else None
+    if f["ragged"] is not None:
+        f["seq_len"] = None
+    f["permute_pages"] = "permutation" in text
+    m = re.search(r"theta=(\d+)", text)
+    if m:
+        f["rope_theta"] = float(m.group(1))
+    first = re.search(r"\b(fp32|fp8|bf16)\b", text).group(1)
+    f["cache_dtype"] = first
+    if "bf16 output" in text:
+        f["out_dtype"] = "bf16"
+    return f
+
+
+def test_configs_match_the_workload_specification():
+    """Every field of workloads.CONFIGS that the workload text states: batch,
+    context or ragged range, query tokens, heads, d_c, d_R, dtypes, page
+    permutation, and the softmax scale 1/sqrt(192) of the 128-head workloads
+    (the tiny model's 1/sqrt(64 + 16) by the same rule)."""
+    spec = _spec()
+    tiny = _parse(spec["tiny"], {"q_len": 1, "out_dtype": "fp32"})
+    c2 = _parse(spec["c2"], {"out_dtype": "bf16", "d_head": 128})
+    c3 = _parse(spec["c3"], {k: c2[k] for k in ("q_len", "n_heads", "d_c", "d_rope", "out_dtype",
+                                                 "scale_sq", "d_head")})
+    c4 = _parse(spec["c4"], {k: c2[k] for k in ("q_len", "out_dtype", "scale_sq", "d_head")})
+    c5 = _parse(spec["c5"], {k: c2[k] for k in ("scale_sq", "d_head")})
+    parsed = {"tiny": tiny, "c2": c2, "c3": c3, "c4": c4, "c5": c5}
+    assert (tiny["batch"], tiny["seq_len"], tiny["n_heads"], tiny["d_head"], tiny["d_c"],
+            tiny["d_rope"], tiny["d_model"], tiny["rope_theta"]) == (1, 256, 8, 64, 64, 16, 512, 10000.0)
+    assert c2["scale_sq"] == 192 and c5["q_len"] == 2 and c4["ragged"] == (512, 16384)
+    for name, f in parsed.items():
+        cfg = wl.CONFIGS[name]
+        for key in ("batch", "seq_len", "q_len", "n_heads", "d_c", "d_rope", "cache_dtype",
+                    "out_dtype", "ragged", "permute_pages", "d_head"):
+            assert getattr(cfg, key) == f[key], (name, key, getattr(cfg, key), f[key])
+        if name == "tiny":
+            assert cfg.d_model == f["d_model"] and cfg.rope_theta == f["rope_theta"]
+            assert cfg.softmax_scale == 1.0 / math.sqrt(f["d_head"] + f["d_rope"]) == 1.0 / math.sqrt(80)
+        else:
+            assert cfg.softmax_scale == 1.0 / math.sqrt(f["scale_sq"]) == 1.0 / math.sqrt(192)
