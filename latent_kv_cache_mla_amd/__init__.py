@@ -11,6 +11,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch first: the library then binds to the HIP runtime torch has loaded. A
+# library loaded before torch would bring in a second HIP runtime (the
+# system's), and kernels launched through it would not see the device that
+# torch's allocations live on.
+import torch  # noqa: F401,E402
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 

@@ -75,7 +75,8 @@ mla_status make_plan(const mla_decode_desc* d, DecodePlan* p) {
   p->part_bf16 = (p->path == Path::Mfma && d->out_dtype == MLA_BF16) ? 1 : 0;
   p->plan_off = 0;
   p->opart_off = align256(sizeof(int32_t) * (static_cast<size_t>(d->batch) + 1));
-  p->lse_off = align256(p->opart_off + sizeof(float) * static_cast<size_t>(p->slots) * rows * d->d_c);
+  const size_t part_elem = p->part_bf16 ? 2 : 4;   // bytes per partial element
+  p->lse_off = align256(p->opart_off + part_elem * static_cast<size_t>(p->slots) * rows * d->d_c);
   p->lsum_off = align256(p->lse_off + sizeof(float) * static_cast<size_t>(p->slots) * rows);
   p->total = align256(p->lsum_off + sizeof(float) * static_cast<size_t>(p->slots) * rows);
   return MLA_OK;

@@ -214,3 +214,15 @@ def test_wait_states_after_inline_matrix_ops_cover_the_hazard(tmp_path):
     assert 0 < needed <= 16, needed
     kernel = open(os.path.join(ROOT, "latent_kv_cache_mla_amd", "csrc", "decode_mfma.hip")).read()
     assert 'v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\\n\\ts_nop 7\\n\\ts_nop 7' in kernel
+
+
+def test_one_hip_runtime_whatever_the_import_order(tmp_path):
+    """Importing the binding before torch must not load a second HIP runtime
+    (the binding loads torch's first, and libmla then binds to it)."""
+    code = ("import latent_kv_cache_mla_amd, torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(paths)); print(sorted(paths))\n")
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.splitlines()[0] == "1", r.stdout
+
