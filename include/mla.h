@@ -161,6 +161,25 @@ mla_status mla_decode_partial(const mla_decode_desc* d, const void* q_abs, const
 mla_status mla_decode_combine(const mla_decode_desc* d, void* workspace, size_t workspace_bytes,
                               void* o_latent, float* lse_out, void* stream);
 
+/* The same decode with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture that must not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation). Instead
+ * of a caller-owned workspace it uses a fixed device array built into the
+ * library: mla_decode_noalloc_max_workspace() bytes (72 MiB) on each GPU the
+ * library runs on, held until the process ends. It allocates nothing and
+ * calls no allocating routine. A call whose descriptor needs more than that
+ * (mla_decode_workspace_size) returns MLA_ERR_WORKSPACE_TOO_SMALL before any
+ * launch. The plan is formed on every call (plan_ready is ignored). Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from several threads without ordering) race
+ * and give wrong results; order them on one stream. Other arguments and
+ * results as in mla_decode. */
+mla_status mla_decode_noalloc(const mla_decode_desc* d, const void* q_abs, const void* q_rope,
+                              const void* cache, const float* cache_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale,
+                              void* o_latent, float* lse_out, void* stream);
+size_t mla_decode_noalloc_max_workspace(void);
+
 /* Debug check of device contents (synchronises `stream`, copies to host):
  * every page id a sequence uses is in [0, n_pages), and every length is in
  * [0, 64 * max_blocks_per_seq]. Returns MLA_ERR_BAD_CONTENTS on the first

@@ -67,6 +67,8 @@ _SIGS = {
     "mla_decode_plan": (_I, [_DESC, _P, _P, _S, _P]),
     "mla_decode": (_I, [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _S, _P]),
     "mla_decode_partial": (_I, [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _S, _P]),
+    "mla_decode_noalloc": (_I, [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "mla_decode_noalloc_max_workspace": (_S, []),
     "mla_decode_combine": (_I, [_DESC, _P, _S, _P, _P, _P]),
     "mla_decode_validate": (_I, [_DESC, _P, _P, ctypes.c_int64, _P]),
     "mla_fold_query": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
@@ -195,6 +197,24 @@ def mla_decode(desc, q_abs, q_rope, cache, cache_scale, block_table, seq_lens, s
                           _ptr(o_latent), _ptr(lse_out), _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream)),
            "mla_decode")
+
+
+def mla_decode_noalloc(desc, q_abs, q_rope, cache, cache_scale, block_table, seq_lens, scale,
+                       o_latent, lse_out, stream=None):
+    for t, n in ((q_abs, "q_abs"), (q_rope, "q_rope"), (cache, "cache"), (cache_scale, "cache_scale"),
+                 (block_table, "block_table"), (seq_lens, "seq_lens"), (o_latent, "o_latent"),
+                 (lse_out, "lse_out")):
+        _dev(t, n)
+    _check_decode_buffers(desc, "mla_decode_noalloc", q_abs, q_rope, block_table, seq_lens,
+                          o_latent, lse_out)
+    _check(lib.mla_decode_noalloc(ctypes.byref(desc), _ptr(q_abs), _ptr(q_rope), _ptr(cache),
+                                  _ptr(cache_scale), _ptr(block_table), _ptr(seq_lens),
+                                  float(scale), _ptr(o_latent), _ptr(lse_out), _stream(stream)),
+           "mla_decode_noalloc")
+
+
+def mla_decode_noalloc_max_workspace():
+    return lib.mla_decode_noalloc_max_workspace()
 
 
 def mla_decode_partial(desc, q_abs, q_rope, cache, cache_scale, block_table, seq_lens, scale,

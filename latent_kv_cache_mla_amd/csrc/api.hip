@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -186,6 +187,66 @@ mla_status mla_decode(const mla_decode_desc* d, const void* q_abs, const void* q
   s = run_partial(a, st);
   if (s != MLA_OK) return s;
   return launch_combine(a, st);
+}
+
+// ---- the allocation-free decode -----------------------------------------
+// Its workspace is this file-scope device array (one per GPU, alive until the
+// process ends). Host code never uses the array's name as an address: the
+// device address of each GPU's copy is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t{72} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure,
+// with the last error set).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(MLA_ERR_HIP, "mla_decode_noalloc: no current device (or device id >= %d)", kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      fail(MLA_ERR_HIP, "mla_decode_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+size_t mla_decode_noalloc_max_workspace(void) { return kScratchBytes; }
+
+mla_status mla_decode_noalloc(const mla_decode_desc* d, const void* q_abs, const void* q_rope,
+                              const void* cache, const float* cache_scale,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale,
+                              void* o_latent, float* lse_out, void* stream) {
+  clear_error();
+  DecodePlan p;
+  mla_status s = make_plan(d, &p);
+  if (s != MLA_OK) return s;
+  if (p.total > kScratchBytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "mla_decode_noalloc: this call needs %zu bytes of workspace, above the fixed "
+                "%zu-byte device scratch array (use mla_decode with a workspace)",
+                p.total, kScratchBytes);
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return MLA_ERR_HIP;
+  // the plan in the shared array may belong to another call: always form it
+  mla_decode_desc dd = *d;
+  dd.plan_ready = 0;
+  return mla_decode(&dd, q_abs, q_rope, cache, cache_scale, block_table, seq_lens, scale,
+                    o_latent, lse_out, ws, kScratchBytes, stream);
 }
 
 mla_status mla_decode_partial(const mla_decode_desc* d, const void* q_abs, const void* q_rope,

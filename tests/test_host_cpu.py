@@ -226,3 +226,20 @@ def test_one_hip_runtime_whatever_the_import_order(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.splitlines()[0] == "1", r.stdout
 
+
+def test_noalloc_decode_rejects_calls_above_its_array(m):
+    """mla_decode_noalloc refuses, on the host and before any launch, a
+    descriptor whose workspace exceeds its fixed device array; the five
+    workloads all fit."""
+    import ctypes
+    big = m.decode_desc(4096, 2, 128, 512, 64, 64, "bf16", "bf16", "bf16")
+    assert m.mla_decode_workspace_size(big) > m.mla_decode_noalloc_max_workspace()
+    dummy = ctypes.c_void_p(256)   # never dereferenced: the size check comes first
+    st = m.lib.mla_decode_noalloc(ctypes.byref(big), dummy, dummy, dummy, None, dummy, dummy,
+                                  ctypes.c_float(0.1), dummy, None, None)
+    assert st == m.MLA_ERR_WORKSPACE_TOO_SMALL, m.mla_last_error()
+    assert "scratch" in m.mla_last_error()
+    for B, q, S, dt in ((32, 1, 4096, "bf16"), (4, 1, 32768, "bf16"), (64, 1, 16384, "bf16"),
+                        (128, 2, 8192, "fp8")):
+        d = m.decode_desc(B, q, 128, 512, 64, (S + 63) // 64, dt, "bf16", "bf16")
+        assert m.mla_decode_workspace_size(d) <= m.mla_decode_noalloc_max_workspace()
