@@ -260,6 +260,91 @@ mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float
                             void* q_abs, void* q_rope, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ---- prefill: the unabsorbed layer over whole prompts -------------------
+ *
+ * Processing all positions of a prompt at once is bound by arithmetic, and
+ * there the layer keeps the unabsorbed form: the latent is expanded into
+ * per-head keys and values ([LLMsBlog] opening section and "Hardware
+ * Trade-offs and Tensor Parallelism"; [Mishra] "Step 2: absorb the
+ * up-projections", last paragraph). Every product is bf16 on the matrix
+ * cores with fp32 accumulation; intermediate activations are rounded to
+ * bf16 between products. */
+
+/* bf16 matrix-core GEMM, the building block of the prefill projections:
+ * C[m, n] = sum_k A[m, k] B[n, k]. A device bf16 [M, K] (row stride lda),
+ * B device bf16 [N, K] (row stride ldb: a weight stored [out, in]), C device
+ * [M, N] (row stride ldc) in c_dtype (MLA_FP32 | MLA_BF16, rounded to nearest
+ * even). K, lda and ldb must be multiples of 8 and A, B 16-byte aligned.
+ * splits > 1 cuts K into that many pieces for skinny M (fp32 partial tiles in
+ * `partial`, mla_gemm_bf16_partial_size bytes, summed in split order:
+ * deterministic). */
+mla_status mla_gemm_bf16(int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, int32_t c_dtype,
+                         int32_t splits, float* partial, void* stream);
+size_t mla_gemm_bf16_partial_size(int32_t M, int32_t N, int32_t K, int32_t splits);
+
+typedef struct mla_prefill_desc {
+  int32_t batch;        /* sequences, >= 1 */
+  int32_t max_seq_len;  /* >= every sequence's length (sizes the launch grid) */
+  int32_t d_model;      /* d: width of h and of the output */
+  int32_t n_heads;      /* n_h */
+  int32_t d_head;       /* d_h: per-head content query/key width = value width */
+  int32_t d_rope;       /* d_R: rope width (shared key, per-head query) */
+  int32_t d_c;          /* latent width */
+  int32_t d_cq;         /* query latent width, or 0: queries projected from h */
+  float rope_theta;     /* RoPE base (interleaved pairs, angle pos * theta^(-2k/d_R)) */
+} mla_prefill_desc;
+
+/* Weights of one layer, device bf16, each stored [out, in] row-major with
+ * head i owning rows [i*width, (i+1)*width) of its block:
+ *   W_DKVR [d_c + d_R, d]              W^DKV rows, then W^KR rows
+ *   W_DQ   [d_cq, d] (NULL if d_cq = 0)
+ *   W_UQR  [n_h*d_h + n_h*d_R, d_in]   W^UQ rows, then W^QR rows (d_in = d_cq or d)
+ *   W_UKV  [2*n_h*d_h, d_c]            W^UK rows, then W^UV rows
+ *   W_O    [d, n_h*d_h]                                                    */
+typedef struct mla_prefill_weights {
+  const void* W_DKVR;
+  const void* W_DQ;
+  const void* W_UQR;
+  const void* W_UKV;
+  const void* W_O;
+} mla_prefill_weights;
+
+/* Causal attention of the expanded form ([Zhang] "Value absorption": scores
+ * (q^C_i . k^C_{j,i} + q^R_i . k^R_j) * scale, softmax over positions j <= t
+ * of the same sequence, o = sum_j a_j v_{j,i}). Built for
+ * (d_h, d_R) in {(128, 64), (64, 16), (64, 32), (128, 0)}.
+ * Rows are tokens: T = cu_seqlens[batch] rows, sequence b = rows
+ * [cu_seqlens[b], cu_seqlens[b+1]) (device int32 [batch + 1]).
+ * q [T, ldq] bf16: head i's content query at columns [i*d_h, (i+1)*d_h);
+ * q_rope [T, ldqr]: head i's rotated rope query at [i*d_R, (i+1)*d_R);
+ * k [T, ldk]: head i's content key at [i*d_h, ...); k_rope [T, ldkr]: the
+ * shared rotated rope key at [0, d_R); v [T, ldv]: head i's value at
+ * [i*d_h, ...); o [T, ldo] bf16 output, head i at [i*d_h, ...); lse device
+ * fp32 [n_h, T] (natural log of sum_j exp(score_j)) or NULL. scale > 0.
+ * Row strides are multiples of 8 elements and inputs 16-byte aligned. */
+mla_status mla_prefill_attention(const mla_prefill_desc* d, int64_t T, const void* q, int64_t ldq,
+                                 const void* q_rope, int64_t ldqr, const void* k, int64_t ldk,
+                                 const void* k_rope, int64_t ldkr, const void* v, int64_t ldv,
+                                 const int32_t* cu_seqlens, float scale, void* o, int64_t ldo,
+                                 float* lse, void* stream);
+
+/* The whole unabsorbed layer for T prompt tokens (the steps are listed in
+ * the source; [Mishra] "Step 1", "Step 4"; [Zhang] "The definitions",
+ * "Decoupled RoPE", "Value absorption"):
+ * h device bf16 [T, d]; cu_seqlens as above; positions device int32 [T]
+ * (RoPE position of each token, normally its index in its sequence);
+ * scale normally 1/sqrt(d_h + d_R); out device fp32 [T, d];
+ * latent device fp32 [T, d_c + d_R] or NULL: the cached row of each token
+ * (c_t, then k^R_t rotated), ready for mla_cache_write-style storage;
+ * lse device fp32 [n_h, T] or NULL; workspace >= mla_prefill_workspace_size
+ * bytes, 256-byte aligned. */
+size_t mla_prefill_workspace_size(const mla_prefill_desc* d, int64_t T);
+mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T,
+                       const int32_t* cu_seqlens, const int32_t* positions,
+                       const mla_prefill_weights* w, float scale, float* out, float* latent,
+                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Cached bytes per token and layer for a cache dtype: FP32 4*(d_c+d_rope);
  * BF16 2*(d_c+d_rope); FP8 d_c + 2*d_rope + 4 (codes, bf16 rope key, fp32
  * scale). With bf16, d_c 512 and d_rope 64 this is 2*576 bytes

@@ -50,6 +50,16 @@ class MlaDecodeDesc(ctypes.Structure):
         "num_partitions", "plan_ready", "flags")]
 
 
+class MlaPrefillDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "max_seq_len", "d_model", "n_heads", "d_head", "d_rope", "d_c", "d_cq")] + \
+        [("rope_theta", ctypes.c_float)]
+
+
+class MlaPrefillWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("W_DKVR", "W_DQ", "W_UQR", "W_UKV", "W_O")]
+
+
 class MlaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -83,6 +93,15 @@ _SIGS = {
     "mla_absorb_query": (_I, [_P, _I, _I, _P, _P, _I, _I, _I, ctypes.c_float, _P, _I, _P, _P,
                               _P, _S, _P]),
     "mla_cache_bytes_per_token": (_S, [_I, _I, _I]),
+    "mla_gemm_bf16": (_I, [_I, _I, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64,
+                           _I, _I, _P, _P]),
+    "mla_gemm_bf16_partial_size": (_S, [_I, _I, _I, _I]),
+    "mla_prefill_attention": (_I, [ctypes.POINTER(MlaPrefillDesc), ctypes.c_int64, _P, ctypes.c_int64,
+                                   _P, ctypes.c_int64, _P, ctypes.c_int64, _P, ctypes.c_int64, _P,
+                                   ctypes.c_int64, _P, ctypes.c_float, _P, ctypes.c_int64, _P, _P]),
+    "mla_prefill_workspace_size": (_S, [ctypes.POINTER(MlaPrefillDesc), ctypes.c_int64]),
+    "mla_prefill": (_I, [ctypes.POINTER(MlaPrefillDesc), _P, ctypes.c_int64, _P, _P,
+                         ctypes.POINTER(MlaPrefillWeights), ctypes.c_float, _P, _P, _P, _P, _S, _P]),
     "mla_status_string": (ctypes.c_char_p, [_I]),
     "mla_last_error": (ctypes.c_char_p, []),
     "mla_version": (_I, []),
@@ -296,6 +315,72 @@ def mla_absorb_query(x, T, d_in, W_qabs, W_QR, n_h, d_c, d_rope, theta, position
                                 _ptr(q_rope), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream)),
            "mla_absorb_query")
+
+
+def mla_gemm_bf16(A, B, C, splits=1, partial=None, stream=None):
+    """C = A B^T for bf16 A [M, K], B [N, K] (row-major, possibly strided
+    rows); C [M, N] fp32 or bf16."""
+    for t, n in ((A, "A"), (B, "B"), (C, "C"), (partial, "partial")):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N) or A.stride(1) != 1 or B.stride(1) != 1 \
+            or C.stride(1) != 1:
+        raise ValueError("mla_gemm_bf16: shapes or layouts do not match")
+    import torch
+    cdt = MLA_BF16 if C.dtype == torch.bfloat16 else MLA_FP32
+    _check(lib.mla_gemm_bf16(M, N, K, _ptr(A), A.stride(0), _ptr(B), B.stride(0), _ptr(C), C.stride(0),
+                             cdt, splits, _ptr(partial), _stream(stream)), "mla_gemm_bf16")
+
+
+def mla_gemm_bf16_partial_size(M, N, K, splits):
+    return lib.mla_gemm_bf16_partial_size(M, N, K, splits)
+
+
+def prefill_desc(batch, max_seq_len, d_model, n_heads, d_head, d_rope, d_c, d_cq=0,
+                 rope_theta=10000.0) -> MlaPrefillDesc:
+    return MlaPrefillDesc(batch, max_seq_len, d_model, n_heads, d_head, d_rope, d_c, d_cq,
+                          float(rope_theta))
+
+
+def mla_prefill_attention(desc, T, q, ldq, q_rope, ldqr, k, ldk, k_rope, ldkr, v, ldv, cu_seqlens,
+                          scale, o, ldo, lse=None, stream=None):
+    for t, n in ((q, "q"), (q_rope, "q_rope"), (k, "k"), (k_rope, "k_rope"), (v, "v"),
+                 (cu_seqlens, "cu_seqlens"), (o, "o"), (lse, "lse")):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+    _check(lib.mla_prefill_attention(ctypes.byref(desc), int(T), _ptr(q), ldq, _ptr(q_rope), ldqr,
+                                     _ptr(k), ldk, _ptr(k_rope), ldkr, _ptr(v), ldv, _ptr(cu_seqlens),
+                                     float(scale), _ptr(o), ldo, _ptr(lse), _stream(stream)),
+           "mla_prefill_attention")
+
+
+def mla_prefill_workspace_size(desc, T):
+    n = lib.mla_prefill_workspace_size(ctypes.byref(desc), int(T))
+    if n == 0:
+        raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_prefill_workspace_size")
+    return n
+
+
+def mla_prefill(desc, h, cu_seqlens, positions, weights, scale, out, latent, lse, workspace,
+                stream=None):
+    """weights: dict with W_DKVR, W_DQ (or None), W_UQR, W_UKV, W_O (bf16 GPU tensors)."""
+    T = h.shape[0]
+    for t, n in ((h, "h"), (cu_seqlens, "cu_seqlens"), (positions, "positions"), (out, "out"),
+                 (latent, "latent"), (lse, "lse"), (workspace, "workspace")):
+        _dev(t, n)
+    for n, t in weights.items():
+        _dev(t, n)
+    w = MlaPrefillWeights(*[None if weights.get(n) is None else weights[n].data_ptr()
+                            for n in ("W_DKVR", "W_DQ", "W_UQR", "W_UKV", "W_O")])
+    _need(out, T * int(desc.d_model) * 4, "out", "mla_prefill")
+    _need(latent, T * (int(desc.d_c) + int(desc.d_rope)) * 4, "latent", "mla_prefill")
+    _need(lse, T * int(desc.n_heads) * 4, "lse", "mla_prefill")
+    _need(h, T * int(desc.d_model) * 2, "h", "mla_prefill")
+    _check(lib.mla_prefill(ctypes.byref(desc), _ptr(h), T, _ptr(cu_seqlens), _ptr(positions),
+                           ctypes.byref(w), float(scale), _ptr(out), _ptr(latent), _ptr(lse),
+                           _ptr(workspace), _nbytes(workspace), _stream(stream)), "mla_prefill")
 
 
 def mla_cache_bytes_per_token(d_c, d_rope, cache_dtype):

@@ -57,6 +57,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// RoPE angle of pair k at position pos, in double precision so that large
+// positions keep their phase (pos * theta^(-2k/d)).
+__device__ __forceinline__ void rope_cs(int pos, int k, int d, double theta, float* c, float* s) {
+  const double ang = static_cast<double>(pos) * pow(theta, -2.0 * k / d);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
 // Effective length of sequence b: negative lengths count as empty and no
 // sequence may extend past its block-table row (so the table is never read
 // out of bounds, whatever the device contents).

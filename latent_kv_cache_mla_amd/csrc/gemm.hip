@@ -79,16 +79,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-// RoPE angle of pair k at position pos, in double precision so that large
-// positions keep their phase (pos * theta^(-2k/d)).
-__device__ __forceinline__ void rope_cs(int pos, int k, int d, double theta, float* c, float* s) {
-  const double ang = static_cast<double>(pos) * pow(theta, -2.0 * k / d);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
-}
-
 // OCP e4m3fn encoding of a finite fp32 value, round to nearest even,
 // saturating to +-448 (written from the format: bias 7, 3 mantissa bits,
 // subnormal step 2^-9).

@@ -85,6 +85,40 @@ struct GemmArgs {
 };
 mla_status launch_gemm(const GemmArgs& g, hipStream_t st);
 
+// bf16 matrix-core GEMM: C[m, n] = sum_k A[m, k] B[n, k] with A [M, K] (row
+// stride lda) and B [N, K] (row stride ldb) in bf16, fp32 accumulation, C in
+// fp32 or bf16 (row stride ldc). K, lda, ldb multiples of 8; A, B 16-byte
+// aligned. splits > 1 cuts K into that many pieces (fp32 partial tiles in
+// `partial` [splits, M, N], summed in split order by a second kernel).
+struct MfmaGemmArgs {
+  int M, N, K;
+  const uint16_t* A; int64_t lda;
+  const uint16_t* B; int64_t ldb;
+  void* C; int64_t ldc; int c_bf16;
+  int splits;
+  float* partial;
+};
+mla_status launch_gemm_bf16(const MfmaGemmArgs& g, hipStream_t st);
+int gemm_bf16_k_per_split(int K, int splits);
+
+// Causal attention of the unabsorbed form over expanded per-head keys and
+// values (bf16 rows; head i of a row at column i * width of its part).
+struct PrefillAttnArgs {
+  const uint16_t* q; int64_t ldq;     // content queries, head i at i * d_h
+  const uint16_t* qr; int64_t ldqr;   // rotated rope queries, head i at i * d_R
+  const uint16_t* k; int64_t ldk;     // expanded content keys, head i at i * d_h
+  const uint16_t* kr; int64_t ldkr;   // the shared rotated rope key
+  const uint16_t* v; int64_t ldv;     // expanded values, head i at i * d_v
+  const int32_t* cu_seqlens;          // [batch + 1] token offsets of the sequences
+  uint16_t* o; int64_t ldo;           // attention output, head i at i * d_v
+  float* lse;                         // [n_heads, T] natural log, or nullptr
+  float c_log2;                       // scale * log2(e), > 0
+  int batch, n_heads, max_seq_len;
+  int64_t T;
+};
+bool prefill_attn_supported(int d_h, int d_rope, int d_v);
+mla_status launch_prefill_attn(const PrefillAttnArgs& a, int d_h, int d_rope, int d_v, hipStream_t st);
+
 // RoPE (interleaved pairs) of rows of width d at per-row positions, in place
 // on fp32 rows with stride ld: x[r, c0 : c0 + d].
 mla_status launch_append_finish(const float* cr, int T, int d_c, int d_rope, float theta,

@@ -1,0 +1,248 @@
+// prefill_attn.hip — causal attention of the unabsorbed MLA form, on the
+// gfx950 matrix cores: every head attends with its expanded content key
+// k^C_{j,i} = W^UK_i c_j, the shared rotated rope key k^R_j, and its expanded
+// value v_{j,i} = W^UV_i c_j ([Mishra] "Multi-head Latent Attention", "Step 1:
+// a low-rank latent" and "Step 4: decoupled RoPE"; [Zhang] "Multi-head latent
+// attention", "Value absorption: weight and sum first, project after": scores
+// (q^C . k^C + q^R . k^R) / sqrt(d_h + d_R), softmax, weighted sum of values).
+// Prefill processes every position of a prompt at once, where the pages note
+// the work is bound by arithmetic rather than by the cache ([LLMsBlog]
+// "Multi-Head Latent Attention: How Low-Rank KV Compression Scales LLM
+// Serving", opening section and "Hardware Trade-offs and Tensor
+// Parallelism"); query position t sees key positions 0..t of its sequence.
+//
+// Workgroup = (query tile of 128 positions, head, sequence); 4 wavefronts of
+// 32 query rows. Keys and values stream through a double-buffered LDS tile of
+// 32 positions, shared by the four wavefronts; the next tile's global loads
+// are in flight while the current one is multiplied.
+//   * scores S^T [32 keys x 32 queries] = K Q^T with v_mfma_f32_32x32x16_bf16,
+//     keys as the M dimension: A = key rows from LDS, B = the wavefront's
+//     queries, held in registers for the whole pass. Each lane then holds 16
+//     keys of one query row: row max and sum are in-lane plus one exchange
+//     between the wavefront halves.
+//   * online softmax in base 2 with a lazy reference: the running max moves
+//     only when a tile's max exceeds it by more than 2^8; then O and the row
+//     sum are rescaled (rare).
+//   * O^T [d_v x 32 queries] += V^T P^T: P^T straight from the score
+//     registers (bf16), V^T read from the row-major value tile with the LDS
+//     transpose load in the key order that matches the score registers.
+// LDS rows are padded (keys: 16 bytes, values: 32 bytes) so that the 16-byte
+// key-fragment reads and the transposed value reads are free of bank
+// conflicts.
+#include "internal.h"
+#include "device_common.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQT = 128;   // query positions per workgroup
+constexpr int kKT = 32;    // key positions per LDS tile
+
+__device__ __forceinline__ s16x4_t tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(static_cast<uintptr_t>(a)));
+}
+
+template <int DC, int DR, int DV>
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
+  constexpr int DQK = DC + DR;
+  static_assert(DQK % 16 == 0 && DC % 8 == 0 && DR % 8 == 0 && DV % 32 == 0, "head dims");
+  constexpr int PK = DQK + 8;    // key row pitch (elements)
+  constexpr int PV = DV + 16;    // value row pitch (elements)
+  constexpr int KTILE = kKT * PK, VTILE = kKT * PV;
+  constexpr int CK = DC / 8, CR = DR / 8, CV = DV / 8;   // 16-byte chunks per row part
+  constexpr int CROW = CK + CR + CV;
+  constexpr int NCH = kKT * CROW;                        // chunks per tile
+  constexpr int NLD = (NCH + 255) / 256;                 // per thread
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][KTILE + VTILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int b = blockIdx.z, head = blockIdx.y;
+  // heavy (late) query tiles first
+  const int n_qt = (a.max_seq_len + kQT - 1) / kQT;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);
+  const int s0 = a.cu_seqlens[b], S = a.cu_seqlens[b + 1] - s0;
+  const int q0 = qt * kQT;
+  if (q0 >= S) return;
+  const int qrow = q0 + 32 * w + l32;          // this lane's query position
+  const int q_last = min(q0 + kQT, S) - 1;     // last query of the workgroup
+  const int n_kt = q_last / kKT + 1;           // key tiles the workgroup needs
+  const int w_last = min(q0 + 32 * w + 31, S - 1);   // this wavefront's last query
+
+  // ---- the wavefront's queries as B fragments: fragment kc holds dims
+  // 16 kc + 8 half .. + 7 of query qrow (rope dims after the content dims)
+  bf16x8_t qf[DQK / 16];
+  {
+    const int64_t t = s0 + min(qrow, S - 1);
+    const uint16_t* qc = a.q + t * a.ldq + static_cast<int64_t>(head) * DC;
+    const uint16_t* qr = a.qr + t * a.ldqr + static_cast<int64_t>(head) * DR;
+#pragma unroll
+    for (int kc = 0; kc < DQK / 16; ++kc) {
+      const int d = 16 * kc + 8 * half;
+      qf[kc] = d < DC ? *reinterpret_cast<const bf16x8_t*>(qc + d)
+                      : *reinterpret_cast<const bf16x8_t*>(qr + (d - DC));
+    }
+  }
+
+  // ---- tile loads: chunk c of a tile is (row c / CROW, part of the row)
+  uint4 st[NLD];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int c = tid + 256 * j;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (c < NCH) {
+        const int row = c / CROW, x = c % CROW;
+        const int key = kt * kKT + row;
+        if (key < S) {
+          const int64_t t = s0 + key;
+          const uint16_t* src;
+          if (x < CK) src = a.k + t * a.ldk + static_cast<int64_t>(head) * DC + 8 * x;
+          else if (x < CK + CR) src = a.kr + t * a.ldkr + 8 * (x - CK);
+          else src = a.v + t * a.ldv + static_cast<int64_t>(head) * DV + 8 * (x - CK - CR);
+          v = *reinterpret_cast<const uint4*>(src);
+        }
+      }
+      st[j] = v;
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int c = tid + 256 * j;
+      if (c < NCH) {
+        const int row = c / CROW, x = c % CROW;
+        uint16_t* dst = x < CK + CR ? &kv_lds[buf][row * PK + 8 * x]
+                                    : &kv_lds[buf][KTILE + row * PV + 8 * (x - CK - CR)];
+        *reinterpret_cast<uint4*>(dst) = st[j];
+      }
+    }
+  };
+
+  f32x16_t o[DV / 32];
+#pragma unroll
+  for (int mb = 0; mb < DV / 32; ++mb) o[mb] = f32x16_t{};
+  float m_run = -INFINITY, l_lane = 0.f;
+  const float c = a.c_log2;
+
+  // LDS byte addresses of this lane's fragments within a tile
+  const uint32_t lds0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&kv_lds[0][0]));
+  const uint32_t tile_bytes = (KTILE + VTILE) * 2;
+  const uint32_t k_off = (l32 * PK + 8 * half) * 2;
+  // transposed value reads: 16-lane group g16, source lane s16 supplies key
+  // row 4 (g16 >> 1) + (s16 >> 2) (+8 for the upper four keys) and dims
+  // 16 (g16 & 1) + 4 (s16 & 3) .. + 3 of a 32-dim block
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const uint32_t v_off = (KTILE + (4 * (g16 >> 1) + (s16 >> 2)) * PV + 16 * (g16 & 1) + 4 * (s16 & 3)) * 2;
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < n_kt;
+    if (more) gload(kt + 1);
+    // tiles that start after the wavefront's last query are fully masked
+    if (kt * kKT <= w_last) {
+      const uint32_t tb = lds0 + buf * tile_bytes;
+      f32x16_t s = f32x16_t{};
+#pragma unroll
+      for (int kc = 0; kc < DQK / 16; ++kc) {
+        const bf16x8_t kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            static_cast<uintptr_t>(tb + k_off + 32 * kc));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s, 0, 0, 0);
+      }
+      // register r holds key kt * 32 + 8 (r / 4) + 4 half + r % 4 of query qrow
+      const int kbase = kt * kKT + 4 * half;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kbase + 8 * (r >> 2) + (r & 3);
+        if (key > qrow || key >= S) s[r] = -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+      if (mx > m_run + 8.0f) {   // lazy reference: rescale only on a large rise
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+#pragma unroll
+        for (int mb = 0; mb < DV / 32; ++mb) o[mb] *= alpha;
+        l_lane *= alpha;
+        m_run = mx;
+      }
+      bf16x8_t pf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_run));
+        const __bf16 pb = static_cast<__bf16>(p);
+        pf[r >> 3][r & 7] = pb;
+        l_lane += static_cast<float>(pb);   // the sum of the weights the products use
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < DV / 32; ++mb) {
+          const uint32_t va = tb + v_off + (16 * kk * PV + 32 * mb) * 2;
+          const s16x4_t lo = tr16(va);
+          const s16x4_t hi = tr16(va + 8 * PV * 2);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[mb], 0, 0, 0);
+        }
+      }
+    }
+    if (more) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l as bf16; register r of o[mb] is dim
+  // 32 mb + 8 (r / 4) + 4 half + r % 4 of query qrow
+  const float l_row = l_lane + __shfl_xor(l_lane, 32, 64);
+  if (qrow < S) {
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    uint16_t* orow = a.o + (s0 + static_cast<int64_t>(qrow)) * a.ldo + static_cast<int64_t>(head) * DV;
+#pragma unroll
+    for (int mb = 0; mb < DV / 32; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u0 = f32_to_bf16(o[mb][4 * j] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[mb][4 * j + 1] * inv)) << 16);
+        const uint32_t u1 = f32_to_bf16(o[mb][4 * j + 2] * inv) | (static_cast<uint32_t>(f32_to_bf16(o[mb][4 * j + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * mb + 8 * j + 4 * half) = make_uint2(u0, u1);
+      }
+    if (a.lse != nullptr && half == 0)
+      a.lse[static_cast<int64_t>(head) * a.T + s0 + qrow] =
+          l_row > 0.f ? (m_run + log2f(l_row)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool prefill_attn_supported(int d_h, int d_rope, int d_v) {
+  return (d_h == 128 && d_rope == 64 && d_v == 128) || (d_h == 64 && d_rope == 16 && d_v == 64) ||
+         (d_h == 64 && d_rope == 32 && d_v == 64) || (d_h == 128 && d_rope == 0 && d_v == 128);
+}
+
+mla_status launch_prefill_attn(const PrefillAttnArgs& a, int d_h, int d_rope, int d_v, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((a.max_seq_len + kQT - 1) / kQT), static_cast<unsigned>(a.n_heads),
+                  static_cast<unsigned>(a.batch));
+  if (d_h == 128 && d_rope == 64 && d_v == 128)
+    hipLaunchKernelGGL((prefill_attn_kernel<128, 64, 128>), grid, dim3(256), 0, st, a);
+  else if (d_h == 64 && d_rope == 16 && d_v == 64)
+    hipLaunchKernelGGL((prefill_attn_kernel<64, 16, 64>), grid, dim3(256), 0, st, a);
+  else if (d_h == 64 && d_rope == 32 && d_v == 64)
+    hipLaunchKernelGGL((prefill_attn_kernel<64, 32, 64>), grid, dim3(256), 0, st, a);
+  else if (d_h == 128 && d_rope == 0 && d_v == 128)
+    hipLaunchKernelGGL((prefill_attn_kernel<128, 0, 128>), grid, dim3(256), 0, st, a);
+  else
+    return fail(MLA_ERR_UNSUPPORTED, "prefill attention is built for (d_h, d_R) in "
+                "{(128, 64), (64, 16), (64, 32), (128, 0)}, got (%d, %d)", d_h, d_rope);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill attention launch: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+}  // namespace mla

@@ -25,8 +25,10 @@ Everything here is plain numpy in float64, written from these pages:
 
 Modules:
   reference  — the unabsorbed definition (O1), the absorbed CPU form (O2),
-               latent attention on given absorbed queries (O3), folds,
-               output projections, RoPE, cache append, query absorption.
+               latent attention on given absorbed queries (O3), one head's
+               causal attention over expanded keys and values (the prefill
+               form), folds, output projections, RoPE, cache append, query
+               absorption.
   formats    — bf16 and fp8 e4m3 decoding/encoding from their definitions.
   closed_forms — per-token cache sizes and operation counts.
 
@@ -36,7 +38,7 @@ identities and closed forms. The RoPE pair layout and rotation direction are
 a free choice (any fixed choice preserves the relative-position property).
 """
 from .reference import (  # noqa: F401
-    rope, softmax, score_scale, mla_unabsorbed, mla_absorbed, latent_attention,
+    rope, softmax, score_scale, expanded_attention, mla_unabsorbed, mla_absorbed, latent_attention,
     fold_query, fold_output, output_projection_merged,
     output_projection_two_stage, cache_append, absorb_query,
 )

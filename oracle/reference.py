@@ -134,6 +134,24 @@ def mla_unabsorbed(model, q_len: int = 1, pos0: int = 0) -> dict:
                 lse=lse, out=out)
 
 
+def expanded_attention(qC, qR, kC, kR, v, scale: float, causal: bool = True) -> dict:
+    """One head of the unabsorbed form over T positions of one sequence:
+    s[t, j] = scale * (qC[t] . kC[j] + qR[t] . kR[j]) for j <= t (all j when
+    not causal), a = softmax(s), o[t] = sum_j a[t, j] v[j]. [Mishra] "Step 4:
+    decoupled RoPE" (the concatenated content and rope parts, whose dot
+    products add); [Zhang] "Value absorption: weight and sum first, project
+    after" (scaled scores, softmax, weighted sum of the values). qC [T, d_h],
+    qR [T, d_R], kC [S, d_h], kR [S, d_R], v [S, d_v]; query t sits at key
+    position t. Returns o [T, d_v] and lse [T] (natural log)."""
+    qC, qR, kC, kR, v = (np.asarray(x, dtype=np.float64) for x in (qC, qR, kC, kR, v))
+    s = scale * (qC @ kC.T + qR @ kR.T)
+    if causal:
+        T, S = s.shape
+        s = np.where(np.arange(S)[None, :] <= np.arange(T)[:, None], s, -np.inf)
+    a = softmax(s)
+    return dict(o=a @ v, lse=_log_sum_exp(s), scores=s, attn=a)
+
+
 # ----------------------------------------------------------------------------
 # folds (offline absorption)
 # ----------------------------------------------------------------------------

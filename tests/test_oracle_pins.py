@@ -397,3 +397,46 @@ def test_unabsorbed_scores_brute_force(golden):
             dot = sum(a * b for a, b in zip(qC + qR, kC + kR[j]))
             want = dot / math.sqrt(g["value"])
             assert abs(r["scores"][0, i, j] - want) <= 1e-12 * max(1.0, abs(want)), (i, j)
+
+
+# ----------------------------------------------------------------------------
+# the expanded (prefill) attention of one head
+# ----------------------------------------------------------------------------
+
+def test_expanded_attention_is_o1_for_every_position():
+    """expanded_attention, fed O1's own per-head query, key and value
+    projections at every position, reproduces O1's per-position head outputs
+    and log-sum-exps (O1 recomputes each position separately, in its own
+    loop)."""
+    cfg = wl.scaled(wl.CONFIGS["tiny"], seq_len=40)
+    model = wl.make_tiny_model(cfg, seed=5)
+    S = cfg.seq_len
+    r1 = oracle.mla_unabsorbed(model, q_len=S)
+    H = model.H.astype(np.float64)
+    c, kR = r1["c"], r1["kR"]
+    dh, dr = cfg.d_head, cfg.d_rope
+    for i in range(cfg.n_heads):
+        qC = H @ np.asarray(model.W_UQ, np.float64)[i * dh:(i + 1) * dh].T
+        qR = oracle.rope(H @ np.asarray(model.W_QR, np.float64)[i * dr:(i + 1) * dr].T, np.arange(S))
+        kC = c @ np.asarray(model.W_UK, np.float64)[i * dh:(i + 1) * dh].T
+        v = c @ np.asarray(model.W_UV, np.float64)[i * dh:(i + 1) * dh].T
+        e = oracle.expanded_attention(qC, qR, kC, kR, v, oracle.score_scale(dh, dr))
+        assert np.max(np.abs(e["o"] - r1["o_heads"][:, i])) < 1e-12
+        assert np.max(np.abs(e["lse"] - r1["lse"][:, i])) < 1e-12
+
+
+def test_expanded_attention_brute_force():
+    """Three positions, written out: position t weighs values 0..t by the
+    exponentials of its scaled scores, normalised."""
+    rng = np.random.default_rng(3)
+    qC, kC = rng.standard_normal((3, 4)), rng.standard_normal((3, 4))
+    qR, kR = rng.standard_normal((3, 2)), rng.standard_normal((3, 2))
+    v = rng.standard_normal((3, 5))
+    sc = 0.7
+    r = oracle.expanded_attention(qC, qR, kC, kR, v, sc)
+    for t in range(3):
+        e = [math.exp(sc * (sum(qC[t] * kC[j]) + sum(qR[t] * kR[j]))) for j in range(t + 1)]
+        want = sum(e[j] * v[j] for j in range(t + 1)) / sum(e)
+        assert np.max(np.abs(r["o"][t] - want)) < 1e-13
+        assert abs(r["lse"][t] - math.log(sum(e))) < 1e-13
+    assert np.allclose(r["o"][0], v[0], atol=0, rtol=0)   # position 0 sees only itself

@@ -314,3 +314,88 @@ def make_tiny_model(cfg: DecodeConfig | None = None, seed: int | None = None,
     H = rng.standard_normal((S, d)).astype(np.float32)
     W_DQ = w(d_cq, d) if d_cq > 0 else None
     return TinyModel(cfg, W_DKV, W_KR, W_UQ, W_QR, W_UK, W_UV, W_O, H, W_DQ)
+
+
+# ----------------------------------------------------------------------------
+# prefill (the unabsorbed layer over whole prompts)
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    """A prompt batch for the unabsorbed layer. Widths of prefill-ds follow
+    DeepSeek-V2 as zhangchitc.github.io "Multi-head latent attention",
+    section "The definitions: project down, then up", gives them (d 5120,
+    query latent 1536, latent 512, 128 heads of 128) with the 64-lane rope
+    key of section "Decoupled RoPE"."""
+    name: str
+    seq_lens: tuple
+    d_model: int
+    n_heads: int
+    d_head: int
+    d_rope: int
+    d_c: int
+    d_cq: int
+    seed: int
+    rope_theta: float = 10000.0
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.seq_lens))
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d_head + self.d_rope)
+
+    def as_decode_config(self) -> DecodeConfig:
+        return DecodeConfig(self.name, len(self.seq_lens), 1, self.n_heads, self.d_c, self.d_rope,
+                            "fp32", "fp32", self.T, seed=self.seed, d_head=self.d_head,
+                            d_model=self.d_model, rope_theta=self.rope_theta)
+
+
+PREFILL_CONFIGS = {
+    # the tiny model's widths, one prompt of 256
+    "prefill-tiny": PrefillConfig("prefill-tiny", (256,), 512, 8, 64, 16, 64, 0, seed=11),
+    # DeepSeek head widths, fewer heads, query compression, two ragged prompts
+    "prefill-mid": PrefillConfig("prefill-mid", (700, 333), 1024, 16, 128, 64, 512, 384, seed=12),
+    # DeepSeek-V2 widths, one prompt of 4096
+    "prefill-ds": PrefillConfig("prefill-ds", (4096,), 5120, 128, 128, 64, 512, 1536, seed=13),
+}
+
+
+def bf16_round(x) -> np.ndarray:
+    """Values rounded to bf16 (RNE), returned as float32 (storage format)."""
+    return bf16_bits_as_f32(to_bf16_bits(x))
+
+
+def make_prefill_model(pcfg: PrefillConfig) -> TinyModel:
+    """Weights N(0, 0.02^2) and hidden states N(0, 1) drawn as make_tiny_model
+    does (all prompts' rows in one H, in batch order), every array rounded to
+    bf16: the values the bf16 prefill path consumes."""
+    m = make_tiny_model(pcfg.as_decode_config(), seq_len=pcfg.T, d_cq=pcfg.d_cq)
+    for k, v in list(m.__dict__.items()):
+        if isinstance(v, np.ndarray):
+            setattr(m, k, bf16_round(v))
+    return m
+
+
+def prefill_gpu_layout(model: TinyModel) -> dict:
+    """bf16 bit arrays in the prefill entry point's layout: h and the weights
+    with the blocks one product shares stacked ([W^DKV; W^KR], [W^UQ; W^QR],
+    [W^UK; W^UV])."""
+    out = {
+        "h": to_bf16_bits(model.H),
+        "W_DKVR": to_bf16_bits(np.concatenate([model.W_DKV, model.W_KR], axis=0)),
+        "W_UQR": to_bf16_bits(np.concatenate([model.W_UQ, model.W_QR], axis=0)),
+        "W_UKV": to_bf16_bits(np.concatenate([model.W_UK, model.W_UV], axis=0)),
+        "W_O": to_bf16_bits(model.W_O),
+        "W_DQ": None if model.W_DQ is None else to_bf16_bits(model.W_DQ),
+    }
+    return out
+
+
+def prefill_cu_seqlens(seq_lens) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(seq_lens, dtype=np.int64))]).astype(np.int32)
+
+
+def prefill_positions(seq_lens) -> np.ndarray:
+    return np.concatenate([np.arange(int(s), dtype=np.int32) for s in seq_lens])
