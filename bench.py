@@ -138,6 +138,8 @@ def gpu_clocks():
     """Current shader and memory clocks as rocm-smi reports them (None if it
     cannot be run)."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None   # under the profiler: no child processes
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=20)
@@ -148,12 +150,129 @@ def gpu_clocks():
         return None
 
 
+def prefill_flops(pcfg):
+    """Algorithmic FLOPs of one prefill layer (2 per multiply-add): the five
+    projections over every token, and the causal attention over the expanded
+    keys and values (attended pairs only: position t sees t + 1 positions)."""
+    T, d, nh, dh, dr, dc, dq = (pcfg.T, pcfg.d_model, pcfg.n_heads, pcfg.d_head, pcfg.d_rope, pcfg.d_c,
+                                pcfg.d_cq)
+    din = dq if dq else d
+    gemm = 2 * T * (d * (dc + dr) + (d * dq if dq else 0) + din * nh * (dh + dr) + dc * 2 * nh * dh
+                    + nh * dh * d)
+    pairs = sum(s * (s + 1) // 2 for s in pcfg.seq_lens)
+    attn = 2 * pairs * nh * (dh + dr + dh)
+    return gemm, attn
+
+
+def prefill_main(args):
+    """The unabsorbed layer over a DeepSeek-V2-width prompt batch (bf16 on the
+    matrix cores): TFLOP/s of the whole layer; the roofline covers the
+    attention kernel, timed alone on inputs of the same shapes."""
+    import numpy as np
+    import torch
+    import latent_kv_cache_mla_amd as mla
+    import workloads as wl
+    pc = wl.PREFILL_CONFIGS["prefill-ds"]
+    model = wl.make_prefill_model(pc)
+    lay = wl.prefill_gpu_layout(model)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    T = pc.T
+    d = mla.prefill_desc(len(pc.seq_lens), max(pc.seq_lens), pc.d_model, pc.n_heads, pc.d_head,
+                         pc.d_rope, pc.d_c, pc.d_cq, pc.rope_theta)
+    h = dev(lay["h"])
+    w = {k: (None if v is None else dev(v)) for k, v in lay.items() if k != "h"}
+    ws = torch.empty(mla.mla_prefill_workspace_size(d, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, pc.d_model, device="cuda")
+    cu = torch.from_numpy(wl.prefill_cu_seqlens(pc.seq_lens)).cuda()
+    pos = torch.from_numpy(wl.prefill_positions(pc.seq_lens)).cuda()
+
+    def step(i):
+        mla.mla_prefill(d, h, cu, pos, w, pc.softmax_scale, out, None, None, ws)
+
+    def timed(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    settle(step)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    per = timed(step, args.steps)
+    ms = float(np.median(per))
+    gemm_f, attn_f = prefill_flops(pc)
+    # the attention kernel alone, on bf16 inputs of the layer's shapes
+    nh, dh, dr = pc.n_heads, pc.d_head, pc.d_rope
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q = torch.randn(T, nh * (dh + dr), generator=g, device="cuda").to(torch.bfloat16)
+    kv = torch.randn(T, 2 * nh * dh, generator=g, device="cuda").to(torch.bfloat16)
+    kr = torch.randn(T, dr, generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty(T, nh * dh, dtype=torch.bfloat16, device="cuda")
+
+    def attn(i):
+        mla.mla_prefill_attention(d, T, q, nh * (dh + dr), q[:, nh * dh:], nh * (dh + dr), kv, 2 * nh * dh,
+                                  kr, dr, kv[:, nh * dh:], 2 * nh * dh, cu, pc.softmax_scale, o, nh * dh)
+
+    for i in range(args.warmup):
+        attn(i)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for i in range(args.steps):
+        attn(i)
+    a1.record()
+    torch.cuda.synchronize()
+    attn_ms = a0.elapsed_time(a1) / args.steps
+    tfs = (gemm_f + attn_f) / (ms * 1e-3) / 1e12
+    attn_tfs = attn_f / (attn_ms * 1e-3) / 1e12
+    line = {
+        "metric": "unabsorbed-MLA prefill TFLOP/s (% of bf16 matrix peak), 128 heads, 1 GPU",
+        "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill-ds: one prompt of 4096 tokens, d 5120, query latent 1536, "
+                               "latent 512, 128 heads of 128 + rope 64",
+                   "tokens": T, "flops_projections": gemm_f, "flops_attention": attn_f,
+                   "parallelism": "single GPU"},
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per, q_)), 4) for q_ in (10, 50, 90)],
+        "pct_bf16_mfma_peak": round(100 * tfs / BF16_MFMA_PEAK_TFS, 2),
+        "roofline": {"bound": "mfma", "kernel": "prefill causal attention", "achieved": round(attn_tfs, 2),
+                     "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(attn_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None,
+                     "kernel_ms": round(attn_ms, 5), "algorithmic_flops_per_launch": attn_f},
+        "clocks": gpu_clocks(),
+    }
+    if not args.no_cpu:
+        import dataclasses
+        import oracle
+        t0 = time.perf_counter()
+        done, n = 0, 0
+        for t in range(250, 4096, 250):   # the output at position t uses positions 0..t only
+            sub = dataclasses.replace(model, H=model.H[:t + 1])
+            oracle.mla_unabsorbed(sub, q_len=1)
+            g1, a1_ = prefill_flops(dataclasses.replace(pc, seq_lens=(1,)))
+            done += g1 + 2 * (t + 1) * nh * (dh + dr + dh)
+            n += 1
+        el = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(done / el / 1e12, 6), "unit": "TFLOP/s",
+                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                "sample": f"O1 (fp64 numpy, unabsorbed) at {n} positions of the prompt "
+                                          f"(t = 250, 500, ..., 4000), {el:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT) + ["prefill"])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for 600 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--fp8-math", action="store_true",
@@ -167,6 +286,8 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "prefill":
+        return prefill_main(args)
     import numpy as np
     import torch
     import latent_kv_cache_mla_amd as mla

@@ -158,15 +158,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
             static_cast<uintptr_t>(tb + k_off + 32 * kc));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s, 0, 0, 0);
       }
-      // register r holds key kt * 32 + 8 (r / 4) + 4 half + r % 4 of query qrow
-      const int kbase = kt * kKT + 4 * half;
+      // register r holds key kt * 32 + 8 (r / 4) + 4 half + r % 4 of query
+      // qrow; only a tile that reaches past the wavefront's first query or the
+      // sequence end needs the mask (a wave-uniform test)
+      if (kt * kKT + kKT - 1 > q0 + 32 * w || kt * kKT + kKT > S) {
+        const int kbase = kt * kKT + 4 * half;
+        const int lim = min(qrow + 1, S);   // visible keys: key < lim
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[r] = kbase + 8 * (r >> 2) + (r & 3) < lim ? s[r] : -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbase + 8 * (r >> 2) + (r & 3);
-        if (key > qrow || key >= S) s[r] = -INFINITY;
-        mx = fmaxf(mx, s[r]);
-      }
+      for (int r = 0; r < 16; r += 2)   // scores are finite or -inf: no NaN handling needed
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(s[r]), "v"(s[r + 1]));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
       if (mx > m_run + 8.0f) {   // lazy reference: rescale only on a large rise
         const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
@@ -175,13 +180,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         l_lane *= alpha;
         m_run = mx;
       }
+      // weights in bf16 pairs; the row sum is taken over the bf16 weights the
+      // products use (a dot product of each pair with (1, 1))
       bf16x8_t pf[2];
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -m_run));
-        const __bf16 pb = static_cast<__bf16>(p);
-        pf[r >> 3][r & 7] = pb;
-        l_lane += static_cast<float>(pb);   // the sum of the weights the products use
+      for (int r = 0; r < 16; r += 2) {
+        const bf16x2_t two = {static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[r], c, -m_run))),
+                              static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -m_run)))};
+        pf[r >> 3][r & 7] = two[0];
+        pf[r >> 3][(r & 7) + 1] = two[1];
+        l_lane = __builtin_amdgcn_fdot2_f32_bf16(two, ones, l_lane, false);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
