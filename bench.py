@@ -267,12 +267,89 @@ def prefill_main(args):
     print(json.dumps(line), flush=True)
 
 
+def proj_main(args):
+    """The per-step projections around the decode kernel at DeepSeek-V2
+    widths for 32 decode tokens (fp32 weights on the fp32 matrix cores):
+    absorbed query (W_qabs and W^QR), cache append (W^DKV and W^KR), and the
+    latent-to-model output projection merged (W_ov) and two-stage (W^UV then
+    W^O). Each is weight-stream bound: GB/s of weights read."""
+    import numpy as np
+    import torch
+    import latent_kv_cache_mla_amd as mla
+    T, d, din, nh, dc, dh, dr = 32, 5120, 1536, 128, 512, 128, 64
+    g = torch.Generator(device="cuda").manual_seed(3)
+
+    def rnd(*s, std=0.02):
+        return torch.randn(*s, generator=g, device="cuda") * std
+    x, h = rnd(T, din, std=1.0), rnd(T, d, std=1.0)
+    W_qabs, W_QR = rnd(nh, dc, din), rnd(nh * dr, din)
+    W_DKV, W_KR = rnd(dc, d), rnd(dr, d)
+    W_ov, W_UV, W_O = rnd(d, nh * dc), rnd(nh * dh, dc), rnd(d, nh * dh)
+    o = rnd(T, nh, dc, std=0.05)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    qa = torch.empty(T, nh, dc, dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty(T, nh, dr, dtype=torch.bfloat16, device="cuda")
+    cache = torch.zeros(1, 64, dc + dr, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(T, d, device="cuda")
+    wq = torch.empty(mla.mla_absorb_query_workspace_size(T, din, nh, dc, dr), dtype=torch.uint8, device="cuda")
+    wa = torch.empty(mla.mla_cache_append_workspace_size(T, d, dc, dr), dtype=torch.uint8, device="cuda")
+    wm = torch.empty(mla.mla_output_proj_workspace_size(T, nh, dc, dh, d, 0), dtype=torch.uint8, device="cuda")
+    w2 = torch.empty(mla.mla_output_proj_workspace_size(T, nh, dc, dh, d, 1), dtype=torch.uint8, device="cuda")
+    cases = {
+        "absorb_query": (lambda: mla.mla_absorb_query(x, T, din, W_qabs, W_QR, nh, dc, dr, 1e4, pos,
+                                                      mla.MLA_BF16, qa, qr, wq),
+                         4 * (W_qabs.numel() + W_QR.numel())),
+        "cache_append": (lambda: mla.mla_cache_append(h, T, d, W_DKV, W_KR, dc, dr, 1e4, pos, pos,
+                                                      mla.MLA_BF16, cache, None, wa),
+                         4 * (W_DKV.numel() + W_KR.numel())),
+        "output_proj_merged": (lambda: mla.mla_output_proj(o, mla.MLA_FP32, T, nh, dc, dh, d, 0, W_ov, None,
+                                                           out, wm), 4 * W_ov.numel()),
+        "output_proj_two_stage": (lambda: mla.mla_output_proj(o, mla.MLA_FP32, T, nh, dc, dh, d, 1, W_UV, W_O,
+                                                              out, w2), 4 * (W_UV.numel() + W_O.numel())),
+    }
+    res = {}
+    for name, (fn, wbytes) in cases.items():
+        for _ in range(max(3, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": round(ms, 5), "weight_bytes": int(wbytes),
+                     "gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # the step's projections: absorbed query + cache append + two-stage output
+    step = ["absorb_query", "cache_append", "output_proj_two_stage"]
+    tot_b = sum(res[k]["weight_bytes"] for k in step)
+    tot_ms = sum(res[k]["ms"] for k in step)
+    dom = max(step, key=lambda k: res[k]["ms"])
+    line = {
+        "metric": "decode-step projections weight-stream GB/s (32 tokens, DeepSeek-V2 widths), 1 GPU",
+        "value": round(tot_b / (tot_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tot_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "projections: 32 tokens, d 5120, query latent 1536, 128 heads, d_c 512, "
+                               "d_h 128, d_R 64, fp32 weights", "parallelism": "single GPU"},
+        "projections": res,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": res[dom]["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res[dom]["frac_hbm"], "traffic": None,
+                     "kernel_ms": res[dom]["ms"], "algorithmic_bytes_per_launch": res[dom]["weight_bytes"]},
+        "clocks": gpu_clocks(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT) + ["prefill"])
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT) + ["prefill", "proj"])
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for 600 MB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--fp8-math", action="store_true",
@@ -288,6 +365,8 @@ def main():
 
     if args.config == "prefill":
         return prefill_main(args)
+    if args.config == "proj":
+        return proj_main(args)
     import numpy as np
     import torch
     import latent_kv_cache_mla_amd as mla

@@ -212,9 +212,12 @@ typedef enum mla_proj_mode {
  * o_latent device [T, n_h, d_c] (o_dtype MLA_FP32 | MLA_BF16);
  * MERGED:    W1 = W_ov fp32 [d, n_h*d_c], W2 unused;
  * TWO_STAGE: W1 = W_UV fp32 [n_h*d_h, d_c], W2 = W_O fp32 [d, n_h*d_h];
- * out device fp32 [T, d]. TWO_STAGE needs T*n_h*d_h*4 bytes of workspace
- * (mla_output_proj_workspace_size). */
-size_t mla_output_proj_workspace_size(int32_t T, int32_t n_h, int32_t d_h, int32_t mode);
+ * out device fp32 [T, d]. workspace: mla_output_proj_workspace_size bytes,
+ * 256-byte aligned (TWO_STAGE: the fp32 head outputs W^UV_i o_i; both modes:
+ * fp32 split-K partial tiles for few rows, summed in a fixed order). With
+ * T up to 256 the products run on the fp32 matrix cores. */
+size_t mla_output_proj_workspace_size(int32_t T, int32_t n_h, int32_t d_c, int32_t d_h, int32_t d,
+                                      int32_t mode);
 mla_status mla_output_proj(const void* o_latent, int32_t o_dtype, int32_t T, int32_t n_h,
                            int32_t d_c, int32_t d_h, int32_t d, int32_t mode,
                            const float* W1, const float* W2, float* out,
@@ -237,8 +240,9 @@ mla_status mla_cache_write(const float* rows, int32_t T, int32_t d_c, int32_t d_
 /* Cache append from hidden states: c_t = W^DKV h_t ([Mishra] "Step 1: a
  * low-rank latent") and W^KR h_t, projected in fp32 into the workspace, then
  * mla_cache_write. h device fp32 [T, d]; W_DKV device fp32 [d_c, d];
- * W_KR device fp32 [d_rope, d]; workspace >= mla_cache_append_workspace_size. */
-size_t mla_cache_append_workspace_size(int32_t T, int32_t d_c, int32_t d_rope);
+ * W_KR device fp32 [d_rope, d]; workspace >= mla_cache_append_workspace_size
+ * bytes, 256-byte aligned (the projected rows and split-K partial tiles). */
+size_t mla_cache_append_workspace_size(int32_t T, int32_t d, int32_t d_c, int32_t d_rope);
 mla_status mla_cache_append(const float* h, int32_t T, int32_t d, const float* W_DKV,
                             const float* W_KR, int32_t d_c, int32_t d_rope, float theta,
                             const int32_t* positions, const int32_t* slots,
@@ -252,8 +256,10 @@ mla_status mla_cache_append(const float* h, int32_t T, int32_t d, const float* W
  * W_qabs device fp32 [n_h, d_c, d_in]; W_QR device fp32 [n_h*d_rope, d_in];
  * positions device int32 [T]; q_abs out [T, n_h, d_c], q_rope out
  * [T, n_h, d_rope], both in q_dtype (MLA_FP32 | MLA_BF16); RoPE as in
- * mla_cache_write. workspace >= mla_absorb_query_workspace_size bytes. */
-size_t mla_absorb_query_workspace_size(int32_t T, int32_t n_h, int32_t d_c, int32_t d_rope);
+ * mla_cache_write. workspace >= mla_absorb_query_workspace_size bytes,
+ * 256-byte aligned. */
+size_t mla_absorb_query_workspace_size(int32_t T, int32_t d_in, int32_t n_h, int32_t d_c,
+                                       int32_t d_rope);
 mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float* W_qabs,
                             const float* W_QR, int32_t n_h, int32_t d_c, int32_t d_rope,
                             float theta, const int32_t* positions, int32_t q_dtype,

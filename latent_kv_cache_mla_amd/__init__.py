@@ -83,13 +83,13 @@ _SIGS = {
     "mla_decode_validate": (_I, [_DESC, _P, _P, ctypes.c_int64, _P]),
     "mla_fold_query": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "mla_fold_output": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
-    "mla_output_proj_workspace_size": (_S, [_I, _I, _I, _I]),
+    "mla_output_proj_workspace_size": (_S, [_I, _I, _I, _I, _I, _I]),
     "mla_output_proj": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]),
     "mla_cache_write": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P, _I, _P, _P, _P]),
-    "mla_cache_append_workspace_size": (_S, [_I, _I, _I]),
+    "mla_cache_append_workspace_size": (_S, [_I, _I, _I, _I]),
     "mla_cache_append": (_I, [_P, _I, _I, _P, _P, _I, _I, ctypes.c_float, _P, _P, _I, _P, _P,
                               _P, _S, _P]),
-    "mla_absorb_query_workspace_size": (_S, [_I, _I, _I, _I]),
+    "mla_absorb_query_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "mla_absorb_query": (_I, [_P, _I, _I, _P, _P, _I, _I, _I, ctypes.c_float, _P, _I, _P, _P,
                               _P, _S, _P]),
     "mla_cache_bytes_per_token": (_S, [_I, _I, _I]),
@@ -272,8 +272,8 @@ def mla_fold_output(W_O, W_UV, n_h, d_h, d_c, d, W_ov, stream=None):
                                _stream(stream)), "mla_fold_output")
 
 
-def mla_output_proj_workspace_size(T, n_h, d_h, mode):
-    return lib.mla_output_proj_workspace_size(T, n_h, d_h, mode)
+def mla_output_proj_workspace_size(T, n_h, d_c, d_h, d, mode):
+    return lib.mla_output_proj_workspace_size(T, n_h, d_c, d_h, d, mode)
 
 
 def mla_output_proj(o_latent, o_dtype, T, n_h, d_c, d_h, d, mode, W1, W2, out, workspace=None,
@@ -291,8 +291,8 @@ def mla_cache_write(rows, T, d_c, d_rope, theta, positions, slots, cache_dtype, 
                                _stream(stream)), "mla_cache_write")
 
 
-def mla_cache_append_workspace_size(T, d_c, d_rope):
-    return lib.mla_cache_append_workspace_size(T, d_c, d_rope)
+def mla_cache_append_workspace_size(T, d, d_c, d_rope):
+    return lib.mla_cache_append_workspace_size(T, d, d_c, d_rope)
 
 
 def mla_cache_append(h, T, d, W_DKV, W_KR, d_c, d_rope, theta, positions, slots, cache_dtype,
@@ -304,8 +304,8 @@ def mla_cache_append(h, T, d, W_DKV, W_KR, d_c, d_rope, theta, positions, slots,
            "mla_cache_append")
 
 
-def mla_absorb_query_workspace_size(T, n_h, d_c, d_rope):
-    return lib.mla_absorb_query_workspace_size(T, n_h, d_c, d_rope)
+def mla_absorb_query_workspace_size(T, d_in, n_h, d_c, d_rope):
+    return lib.mla_absorb_query_workspace_size(T, d_in, n_h, d_c, d_rope)
 
 
 def mla_absorb_query(x, T, d_in, W_qabs, W_QR, n_h, d_c, d_rope, theta, positions, q_dtype,

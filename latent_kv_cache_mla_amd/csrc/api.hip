@@ -345,9 +345,18 @@ mla_status mla_fold_output(const float* W_O, const float* W_UV, int32_t n_h, int
   return launch_gemm(g, static_cast<hipStream_t>(stream));
 }
 
-size_t mla_output_proj_workspace_size(int32_t T, int32_t n_h, int32_t d_h, int32_t mode) {
-  if (T < 0 || n_h < 1 || d_h < 1) return 0;
-  return mode == MLA_PROJ_TWO_STAGE ? sizeof(float) * static_cast<size_t>(T) * n_h * d_h : 0;
+namespace {
+size_t a256b(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+size_t max2(size_t a, size_t b) { return a > b ? a : b; }
+}  // namespace
+
+size_t mla_output_proj_workspace_size(int32_t T, int32_t n_h, int32_t d_c, int32_t d_h, int32_t d,
+                                      int32_t mode) {
+  if (T < 0 || n_h < 1 || d_c < 1 || d < 1) return 0;
+  if (mode == MLA_PROJ_MERGED) return a256b(gemm_partial_bytes(1, T, d, n_h * d_c)) + 256;
+  if (mode != MLA_PROJ_TWO_STAGE || d_h < 1) return 0;
+  return a256b(sizeof(float) * static_cast<size_t>(T) * n_h * d_h) +
+         a256b(max2(gemm_partial_bytes(n_h, T, d_h, d_c), gemm_partial_bytes(1, T, d, n_h * d_h))) + 256;
 }
 
 mla_status mla_output_proj(const void* o_latent, int32_t o_dtype, int32_t T, int32_t n_h,
@@ -361,27 +370,34 @@ mla_status mla_output_proj(const void* o_latent, int32_t o_dtype, int32_t T, int
     return fail(MLA_ERR_INVALID_ARGUMENT, "o_dtype must be MLA_FP32 or MLA_BF16");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t K = static_cast<int64_t>(n_h) * d_c;
+  if (mode != MLA_PROJ_MERGED && mode != MLA_PROJ_TWO_STAGE)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "unknown mode %d", mode);
+  if (mode == MLA_PROJ_TWO_STAGE && !W2) return fail(MLA_ERR_INVALID_ARGUMENT, "two-stage projection needs W_O");
+  if (mode == MLA_PROJ_TWO_STAGE && d_h < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "d_h must be >= 1");
+  const size_t need = mla_output_proj_workspace_size(T, n_h, d_c, d_h, d, mode);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", need);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
   if (mode == MLA_PROJ_MERGED) {
     GemmArgs g{};
     g.batch = 1; g.M = T; g.N = d; g.K = static_cast<int>(K);
     g.A = o_latent; g.a_bf16 = o_dtype == MLA_BF16; g.sAb = 0; g.sAm = K; g.sAk = 1;
     g.B = W1; g.sBb = 0; g.sBk = 1; g.sBn = K;
     g.Y = out; g.sYb = 0; g.sYm = d; g.sYn = 1;
-    return launch_gemm(g, st);
+    return launch_gemm(g, st, reinterpret_cast<float*>(ws), workspace_bytes);
   }
-  if (mode != MLA_PROJ_TWO_STAGE) return fail(MLA_ERR_INVALID_ARGUMENT, "unknown mode %d", mode);
-  if (!W2) return fail(MLA_ERR_INVALID_ARGUMENT, "two-stage projection needs W_O");
-  if (d_h < 1) return fail(MLA_ERR_INVALID_ARGUMENT, "d_h must be >= 1");
-  const size_t need = mla_output_proj_workspace_size(T, n_h, d_h, mode);
-  if (workspace_bytes < need || (need > 0 && workspace == nullptr))
-    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", need);
   float* U = static_cast<float*>(workspace);
+  const size_t u_bytes = a256b(sizeof(float) * static_cast<size_t>(T) * n_h * d_h);
+  float* part = reinterpret_cast<float*>(ws + u_bytes);
+  const size_t part_bytes = workspace_bytes - u_bytes;
   GemmArgs g{};
   g.batch = n_h; g.M = T; g.N = d_h; g.K = d_c;
   g.A = o_latent; g.a_bf16 = o_dtype == MLA_BF16; g.sAb = d_c; g.sAm = K; g.sAk = 1;
   g.B = W1; g.sBb = static_cast<int64_t>(d_h) * d_c; g.sBk = 1; g.sBn = d_c;
   g.Y = U; g.sYb = d_h; g.sYm = static_cast<int64_t>(n_h) * d_h; g.sYn = 1;
-  mla_status s = launch_gemm(g, st);
+  mla_status s = launch_gemm(g, st, part, part_bytes);
   if (s != MLA_OK) return s;
   GemmArgs g2{};
   const int64_t K2 = static_cast<int64_t>(n_h) * d_h;
@@ -389,12 +405,13 @@ mla_status mla_output_proj(const void* o_latent, int32_t o_dtype, int32_t T, int
   g2.A = U; g2.a_bf16 = 0; g2.sAb = 0; g2.sAm = K2; g2.sAk = 1;
   g2.B = W2; g2.sBb = 0; g2.sBk = 1; g2.sBn = K2;
   g2.Y = out; g2.sYb = 0; g2.sYm = d; g2.sYn = 1;
-  return launch_gemm(g2, st);
+  return launch_gemm(g2, st, part, part_bytes);
 }
 
-size_t mla_cache_append_workspace_size(int32_t T, int32_t d_c, int32_t d_rope) {
-  if (T < 0 || d_c < 1 || d_rope < 0) return 0;
-  return sizeof(float) * static_cast<size_t>(T) * (d_c + d_rope);
+size_t mla_cache_append_workspace_size(int32_t T, int32_t d, int32_t d_c, int32_t d_rope) {
+  if (T < 0 || d < 1 || d_c < 1 || d_rope < 0) return 0;
+  return a256b(sizeof(float) * static_cast<size_t>(T) * (d_c + d_rope)) +
+         a256b(max2(gemm_partial_bytes(1, T, d_c, d), gemm_partial_bytes(1, T, d_rope, d))) + 256;
 }
 
 mla_status mla_cache_write(const float* rows, int32_t T, int32_t d_c, int32_t d_rope, float theta,
@@ -421,31 +438,39 @@ mla_status mla_cache_append(const float* h, int32_t T, int32_t d, const float* W
   if (!h || !W_DKV || (d_rope > 0 && !W_KR) || !workspace)
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (T < 0 || d < 1 || d_c < 1 || d_rope < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "bad sizes");
-  if (workspace_bytes < mla_cache_append_workspace_size(T, d_c, d_rope))
+  if (workspace_bytes < mla_cache_append_workspace_size(T, d, d_c, d_rope))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* cr = static_cast<float*>(workspace);
+  const size_t cr_bytes = a256b(sizeof(float) * static_cast<size_t>(T) * (d_c + d_rope));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cr_bytes);
+  const size_t part_bytes = workspace_bytes - cr_bytes;
   const int L = d_c + d_rope;
   GemmArgs g{};
   g.batch = 1; g.M = T; g.N = d_c; g.K = d;
   g.A = h; g.a_bf16 = 0; g.sAm = d; g.sAk = 1;
   g.B = W_DKV; g.sBk = 1; g.sBn = d;
   g.Y = cr; g.sYm = L; g.sYn = 1;
-  mla_status s = launch_gemm(g, st);
+  mla_status s = launch_gemm(g, st, part, part_bytes);
   if (s != MLA_OK) return s;
   if (d_rope > 0) {
     GemmArgs g2 = g;
     g2.N = d_rope; g2.B = W_KR; g2.Y = cr + d_c;
-    s = launch_gemm(g2, st);
+    s = launch_gemm(g2, st, part, part_bytes);
     if (s != MLA_OK) return s;
   }
   return mla_cache_write(cr, T, d_c, d_rope, theta, positions, slots, cache_dtype, cache,
                          cache_scale, stream);
 }
 
-size_t mla_absorb_query_workspace_size(int32_t T, int32_t n_h, int32_t d_c, int32_t d_rope) {
-  if (T < 0 || n_h < 1 || d_c < 1 || d_rope < 0) return 0;
-  return sizeof(float) * static_cast<size_t>(T) * n_h * (d_c + d_rope);
+size_t mla_absorb_query_workspace_size(int32_t T, int32_t d_in, int32_t n_h, int32_t d_c,
+                                       int32_t d_rope) {
+  if (T < 0 || d_in < 1 || n_h < 1 || d_c < 1 || d_rope < 0) return 0;
+  return a256b(sizeof(float) * static_cast<size_t>(T) * n_h * (d_c + d_rope)) +
+         a256b(max2(gemm_partial_bytes(n_h, T, d_c, d_in), gemm_partial_bytes(1, T, n_h * d_rope, d_in))) +
+         256;
 }
 
 mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float* W_qabs,
@@ -459,17 +484,22 @@ mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float
     return fail(MLA_ERR_INVALID_ARGUMENT, "bad sizes");
   if (q_dtype != MLA_FP32 && q_dtype != MLA_BF16)
     return fail(MLA_ERR_INVALID_ARGUMENT, "q_dtype must be MLA_FP32 or MLA_BF16");
-  if (workspace_bytes < mla_absorb_query_workspace_size(T, n_h, d_c, d_rope))
+  if (workspace_bytes < mla_absorb_query_workspace_size(T, d_in, n_h, d_c, d_rope))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "workspace too small");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MLA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* qa32 = static_cast<float*>(workspace);
   float* qr32 = qa32 + static_cast<size_t>(T) * n_h * d_c;
+  const size_t q_bytes = a256b(sizeof(float) * static_cast<size_t>(T) * n_h * (d_c + d_rope));
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + q_bytes);
+  const size_t part_bytes = workspace_bytes - q_bytes;
   GemmArgs g{};
   g.batch = n_h; g.M = T; g.N = d_c; g.K = d_in;
   g.A = x; g.a_bf16 = 0; g.sAb = 0; g.sAm = d_in; g.sAk = 1;
   g.B = W_qabs; g.sBb = static_cast<int64_t>(d_c) * d_in; g.sBk = 1; g.sBn = d_in;
   g.Y = qa32; g.sYb = d_c; g.sYm = static_cast<int64_t>(n_h) * d_c; g.sYn = 1;
-  mla_status s = launch_gemm(g, st);
+  mla_status s = launch_gemm(g, st, part, part_bytes);
   if (s != MLA_OK) return s;
   if (d_rope > 0) {
     GemmArgs g2{};
@@ -477,7 +507,7 @@ mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float
     g2.A = x; g2.a_bf16 = 0; g2.sAm = d_in; g2.sAk = 1;
     g2.B = W_QR; g2.sBk = 1; g2.sBn = d_in;
     g2.Y = qr32; g2.sYm = static_cast<int64_t>(n_h) * d_rope; g2.sYn = 1;
-    s = launch_gemm(g2, st);
+    s = launch_gemm(g2, st, part, part_bytes);
     if (s != MLA_OK) return s;
   }
   return launch_query_finish(qa32, qr32, T, n_h, d_c, d_rope, theta, positions, q_dtype, q_abs,

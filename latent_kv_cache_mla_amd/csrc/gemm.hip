@@ -13,6 +13,8 @@
 //     How Low-Rank KV Compression Scales LLM Serving", "Query Key Absorption").
 // All are fp32 with fp32 accumulation through one LDS-tiled strided batched
 // GEMM: these are offline or per-step projections off the attention loop.
+#include <type_traits>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -159,7 +161,10 @@ __global__ __launch_bounds__(256) void append_finish_kernel(const float* __restr
   }
 }
 
-// One block per query token: rotate q^R per head, convert both outputs.
+// Block (token t, slice y of gridDim.y): convert a slice of q_abs, and rotate
+// q^R of the heads of the slice. The rotation of pair k depends only on the
+// token's position, so its cosine and sine are computed once per block (the
+// first d_r / 2 threads, fp64) and shared through LDS.
 template <int QT>
 __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restrict__ qa32,
                                                            const float* __restrict__ qr32, int n_h,
@@ -167,19 +172,25 @@ __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restri
                                                            const int32_t* __restrict__ positions,
                                                            void* __restrict__ q_abs,
                                                            void* __restrict__ q_rope) {
+  __shared__ float cs_lds[2][128];
   const int64_t t = blockIdx.x;
   const int pos = positions[t];
+  const int half = d_r / 2;
+  for (int k = threadIdx.x; k < half; k += 256) rope_cs(pos, k, d_r, theta, &cs_lds[0][k], &cs_lds[1][k]);
+  __syncthreads();
   const int64_t na = static_cast<int64_t>(n_h) * d_c;
-  for (int64_t i = threadIdx.x; i < na; i += 256) {
+  const int64_t per = (na + gridDim.y - 1) / gridDim.y;
+  const int64_t i0 = blockIdx.y * per, i1 = min(na, i0 + per);
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
     const float v = qa32[t * na + i];
     if constexpr (QT == MLA_FP32) static_cast<float*>(q_abs)[t * na + i] = v;
     else static_cast<uint16_t*>(q_abs)[t * na + i] = f32_to_bf16(v);
   }
-  const int half = d_r / 2;
-  for (int i = threadIdx.x; i < n_h * half; i += 256) {
-    const int h = i / half, k = i % half;
-    float c, s;
-    rope_cs(pos, k, d_r, theta, &c, &s);
+  const int hp = (n_h + gridDim.y - 1) / gridDim.y;
+  const int h0 = blockIdx.y * hp, h1 = min(n_h, h0 + hp);
+  for (int i = threadIdx.x; i < (h1 - h0) * half; i += 256) {
+    const int h = h0 + i / half, k = i % half;
+    const float c = cs_lds[0][k], s = cs_lds[1][k];
     const int64_t base = (t * n_h + h) * d_r;
     const float x0 = qr32[base + 2 * k], x1 = qr32[base + 2 * k + 1];
     const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
@@ -193,13 +204,170 @@ __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restri
   }
 }
 
+// ---- the per-step projections: few rows (decode tokens), weights streamed once
+//
+// Y[b][m][n] = sum_k A[b](m, k) W[b](n, k) with A and W contiguous along k
+// (activations [T, K], a weight stored [out, in]). fp32 products on the
+// matrix cores (v_mfma_f32_32x32x2_f32: exact fp32 multiplies, fp32
+// accumulation), so the result keeps the precision of the fp32 weights.
+// Workgroup = 32 rows x 128 outputs (4 wavefronts x 32 outputs) over one
+// split of K; A and W tiles of 32 k go through double-buffered LDS with rows
+// padded to 33 words. Each weight element is read from memory once per row
+// block; split-K (fp32 partial tiles, summed in split order) gives the
+// skinny shapes enough workgroups to stream the weights at full bandwidth.
+typedef float f32x16g __attribute__((ext_vector_type(16)));
+constexpr int kSM = 32, kSN = 128, kSK = 32, kSP = kSK + 1;
+
+template <int A_BF16>
+__global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs g, int splits, int k_per_split,
+                                                          float* __restrict__ partial) {
+  __shared__ float As[2][kSM * kSP];
+  __shared__ float Ws[2][kSN * kSP];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kSN;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kSM;
+  const int bz = blockIdx.z / splits, z = blockIdx.z % splits;
+  const int kb = z * k_per_split, ke = min(g.K, kb + k_per_split);
+  const float* Af = static_cast<const float*>(g.A) + bz * g.sAb;
+  const uint16_t* Ah = static_cast<const uint16_t*>(g.A) + bz * g.sAb;
+  const float* W = g.B + bz * g.sBb;
+  // thread tid stages A element (row tid / 8, k 4 (tid % 8) .. + 3) and W rows
+  // tid / 8 + 32 j (j < 4), k 4 (tid % 8) .. + 3
+  const int r8 = tid >> 3, k4 = (tid & 7) * 4;
+  // two register sets: the loads of stage s + 2 are issued before stage s is
+  // multiplied, so each stage's loads have two stages of MFMAs to arrive
+  float ra[2][4], rw[2][4][4];
+  auto gload = [&](auto SET, int k0) {
+    constexpr int set = decltype(SET)::value;
+    const int64_t m = m0 + r8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = k0 + k4 + i;
+      float v = 0.f;
+      if (m < g.M && k < ke) v = A_BF16 ? bf16_to_f32(Ah[m * g.sAm + k]) : Af[m * g.sAm + k];
+      ra[set][i] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + r8 + 32 * j;
+      const int k = k0 + k4;
+      if (n < g.N && k + 3 < ke) {
+        const float4 v = *reinterpret_cast<const float4*>(W + n * g.sBn + k);
+        rw[set][j][0] = v.x; rw[set][j][1] = v.y; rw[set][j][2] = v.z; rw[set][j][3] = v.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rw[set][j][i] = (n < g.N && k + i < ke) ? W[n * g.sBn + k + i] : 0.f;
+      }
+    }
+  };
+  auto swrite = [&](auto SET, int buf) {
+    constexpr int set = decltype(SET)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) As[buf][r8 * kSP + k4 + i] = ra[set][i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ws[buf][(r8 + 32 * j) * kSP + k4 + i] = rw[set][j][i];
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  f32x16g acc = f32x16g{};
+  if (kb < ke) {
+    gload(S0{}, kb);
+    if (kb + kSK < ke) gload(S1{}, kb + kSK);
+    swrite(S0{}, 0);
+  }
+  __syncthreads();
+  // stage at k0 sits in LDS buffer buf; its successor in register set 1 - SET
+  // (SET alternates with the stage, at compile time through the unrolled pair)
+  auto stage = [&](auto SET, int k0, int buf) {
+    constexpr int set = decltype(SET)::value;
+    if (k0 + 2 * kSK < ke) gload(std::integral_constant<int, set>{}, k0 + 2 * kSK);
+#pragma unroll
+    for (int kk = 0; kk < kSK / 2; ++kk) {
+      const float a = As[buf][l32 * kSP + 2 * kk + half];
+      const float b = Ws[buf][(32 * w + l32) * kSP + 2 * kk + half];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    if (k0 + kSK < ke) swrite(std::integral_constant<int, 1 - set>{}, buf ^ 1);
+    __syncthreads();
+  };
+  for (int k0 = kb; k0 < ke; k0 += 2 * kSK) {
+    stage(S0{}, k0, 0);
+    if (k0 + kSK < ke) stage(S1{}, k0 + kSK, 1);
+  }
+  // register r: row m0 + 8 (r / 4) + 4 half + r % 4, output n0 + 32 w + l32
+  const int64_t n = n0 + 32 * w + l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t m = m0 + 8 * (r >> 2) + 4 * half + (r & 3);
+    if (m >= g.M || n >= g.N) continue;
+    if (splits > 1)
+      partial[((static_cast<int64_t>(z) * g.batch + bz) * g.M + m) * g.N + n] = acc[r];
+    else
+      g.Y[bz * g.sYb + m * g.sYm + n * g.sYn] = acc[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int splits,
+                                                            const float* __restrict__ partial) {
+  const int64_t per = static_cast<int64_t>(g.M) * g.N, total = per * g.batch;
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < total; e += static_cast<int64_t>(gridDim.x) * 256) {
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += partial[z * total + e];
+    const int64_t b = e / per, m = (e % per) / g.N, n = e % g.N;
+    g.Y[b * g.sYb + m * g.sYm + n * g.sYn] = s;
+  }
+}
+
+bool skinny_ok(const GemmArgs& g) {
+  return g.sAk == 1 && g.sBk == 1 && g.sBn % 4 == 0 && g.sBb % 4 == 0 && aligned16(g.B) &&
+         g.M <= 8 * kSM;
+}
+
 }  // namespace
 
-mla_status launch_gemm(const GemmArgs& g, hipStream_t st) {
+int skinny_splits(int batch, int M, int N, int K) {
+  const int64_t base = static_cast<int64_t>(batch) * ((M + kSM - 1) / kSM) * ((N + kSN - 1) / kSN);
+  int64_t s = (4 * kNumCUs + base - 1) / base;
+  const int64_t kmax = (K + 255) / 256;   // at least 256 k per split
+  if (s > kmax) s = kmax;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return static_cast<int>(s);
+}
+
+size_t gemm_partial_bytes(int batch, int M, int N, int K) {
+  const int s = skinny_splits(batch, M, N, K);
+  return s > 1 ? sizeof(float) * static_cast<size_t>(s) * batch * M * N : 0;
+}
+
+mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial, size_t partial_bytes) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return MLA_OK;
-  const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, g.batch);
-  if (grid.y > 65535u || grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, g);
+  if (skinny_ok(g)) {
+    int splits = skinny_splits(g.batch, g.M, g.N, g.K);
+    if (partial == nullptr || gemm_partial_bytes(g.batch, g.M, g.N, g.K) > partial_bytes) splits = 1;
+    const int kps = (g.K + splits - 1) / splits;
+    const int kps_r = (kps + kSK - 1) / kSK * kSK;
+    const int gz = splits > 1 ? (g.K + kps_r - 1) / kps_r : 1;
+    const dim3 grid((g.N + kSN - 1) / kSN, (g.M + kSM - 1) / kSM, static_cast<unsigned>(g.batch * gz));
+    if (grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
+    if (g.a_bf16)
+      hipLaunchKernelGGL(skinny_gemm_kernel<1>, grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    else
+      hipLaunchKernelGGL(skinny_gemm_kernel<0>, grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    if (gz > 1) {
+      const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
+      const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks), dim3(256), 0, st, g, gz,
+                         static_cast<const float*>(partial));
+    }
+  } else {
+    const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, g.batch);
+    if (grid.y > 65535u || grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, g);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return MLA_OK;
@@ -229,12 +397,16 @@ mla_status launch_query_finish(const float* q_abs32, const float* q_rope32, int 
                                int d_c, int d_rope, float theta, const int32_t* positions,
                                int q_dtype, void* q_abs, void* q_rope, hipStream_t st) {
   if (T <= 0) return MLA_OK;
+  if (d_rope > 256) return fail(MLA_ERR_UNSUPPORTED, "query finish: d_rope above 256");
   const double th = theta;
+  // enough blocks to fill the chip: heads are split over gridDim.y
+  const int ny = n_h < 16 ? n_h : 16;
+  const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(ny));
   if (q_dtype == MLA_FP32)
-    hipLaunchKernelGGL(query_finish_kernel<MLA_FP32>, dim3(T), dim3(256), 0, st, q_abs32, q_rope32,
+    hipLaunchKernelGGL(query_finish_kernel<MLA_FP32>, grid, dim3(256), 0, st, q_abs32, q_rope32,
                        n_h, d_c, d_rope, th, positions, q_abs, q_rope);
   else
-    hipLaunchKernelGGL(query_finish_kernel<MLA_BF16>, dim3(T), dim3(256), 0, st, q_abs32, q_rope32,
+    hipLaunchKernelGGL(query_finish_kernel<MLA_BF16>, grid, dim3(256), 0, st, q_abs32, q_rope32,
                        n_h, d_c, d_rope, th, positions, q_abs, q_rope);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "query finish launch: %s", hipGetErrorString(e));

@@ -83,7 +83,13 @@ struct GemmArgs {
   const float* B; int64_t sBb, sBk, sBn;
   float* Y; int64_t sYb, sYm, sYn;
 };
-mla_status launch_gemm(const GemmArgs& g, hipStream_t st);
+// Row counts up to 256 with operands contiguous along k run on the fp32
+// matrix cores with split-K when `partial` holds gemm_partial_bytes (else
+// without splitting); other shapes on an LDS-tiled fp32 vector kernel.
+mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial = nullptr,
+                       size_t partial_bytes = 0);
+size_t gemm_partial_bytes(int batch, int M, int N, int K);
+int skinny_splits(int batch, int M, int N, int K);
 
 // bf16 matrix-core GEMM: C[m, n] = sum_k A[m, k] B[n, k] with A [M, K] (row
 // stride lda) and B [N, K] (row stride ldb) in bf16, fp32 accumulation, C in

@@ -57,7 +57,7 @@ def test_absorb_query(q_dtype):
     dt = torch.float32 if q_dtype == "fp32" else torch.bfloat16
     qa = torch.empty((T, nh, dc), dtype=dt, device="cuda")
     qr = torch.empty((T, nh, dr), dtype=dt, device="cuda")
-    ws = torch.empty(m.mla_absorb_query_workspace_size(T, nh, dc, dr), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(m.mla_absorb_query_workspace_size(T, din, nh, dc, dr), dtype=torch.uint8, device="cuda")
     m.mla_absorb_query(_t(x), T, din, _t(W_qabs), _t(W_QR), nh, dc, dr, 10000.0,
                        torch.from_numpy(pos).cuda(), code, qa, qr, ws)
     torch.cuda.synchronize()
@@ -127,7 +127,7 @@ def _tiny_chain(cfg, cache_dtype, mode):
     qdt = torch.float32 if q_dt == "fp32" else torch.bfloat16
     qa = torch.empty((1, 1, nh, dc), dtype=qdt, device="cuda")
     qr = torch.empty((1, 1, nh, dr), dtype=qdt, device="cuda")
-    ws = torch.empty(m.mla_absorb_query_workspace_size(1, nh, dc, dr), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(m.mla_absorb_query_workspace_size(1, d, nh, dc, dr), dtype=torch.uint8, device="cuda")
     pos_q = torch.tensor([S - 1], dtype=torch.int32, device="cuda")
     m.mla_absorb_query(_t(model.H[S - 1:]), 1, d, A, _t(model.W_QR), nh, dc, dr, cfg.rope_theta,
                        pos_q, m.DTYPE_CODES[q_dt], qa, qr, ws)
@@ -139,7 +139,7 @@ def _tiny_chain(cfg, cache_dtype, mode):
         cache = torch.zeros((n_pages, 64, dc + dr), dtype=qdt, device="cuda")
         sc = None
     pos = torch.arange(S, dtype=torch.int32, device="cuda")
-    wa = torch.empty(m.mla_cache_append_workspace_size(S, dc, dr), dtype=torch.uint8, device="cuda")
+    wa = torch.empty(m.mla_cache_append_workspace_size(S, d, dc, dr), dtype=torch.uint8, device="cuda")
     m.mla_cache_append(_t(model.H), S, d, _t(model.W_DKV), _t(model.W_KR), dc, dr, cfg.rope_theta,
                        pos, pos, m.DTYPE_CODES[cache_dtype], cache, sc, wa)
     desc = m.decode_desc(1, 1, nh, dc, dr, n_pages, cache_dtype, q_dt, "fp32")
@@ -149,12 +149,13 @@ def _tiny_chain(cfg, cache_dtype, mode):
     sl = torch.tensor([S], dtype=torch.int32, device="cuda")
     m.mla_decode(desc, qa, qr, cache, sc, bt, sl, cfg.softmax_scale, o, None, wsd)
     out = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    wp = torch.empty(m.mla_output_proj_workspace_size(1, nh, dc, dh, d, mode), dtype=torch.uint8,
+                     device="cuda")
     if mode == m.MLA_PROJ_MERGED:
         F = torch.empty((d, nh * dc), dtype=torch.float32, device="cuda")
         m.mla_fold_output(_t(model.W_O), _t(model.W_UV), nh, dh, dc, d, F)
-        m.mla_output_proj(o, m.MLA_FP32, 1, nh, dc, dh, d, mode, F, None, out)
+        m.mla_output_proj(o, m.MLA_FP32, 1, nh, dc, dh, d, mode, F, None, out, wp)
     else:
-        wp = torch.empty(m.mla_output_proj_workspace_size(1, nh, dh, mode), dtype=torch.uint8, device="cuda")
         m.mla_output_proj(o, m.MLA_FP32, 1, nh, dc, dh, d, mode, _t(model.W_UV), _t(model.W_O), out, wp)
     torch.cuda.synchronize()
     return model, o.cpu().numpy().astype(np.float64), out.cpu().numpy().astype(np.float64)
@@ -182,3 +183,88 @@ def test_tiny_model_end_to_end_quantised_cache(cache_dtype):
     model, o, out = _tiny_chain(cfg, cache_dtype, 1)
     r1 = oracle.mla_unabsorbed(model)
     H.assert_close(out, r1["out"], cache_dtype, f"tiny-out-{cache_dtype}")
+
+
+# ----------------------------------------------------------------------------
+# the per-step projections at DeepSeek-V2 widths (32 decode tokens)
+# ----------------------------------------------------------------------------
+
+DS = dict(T=32, d=5120, d_in=1536, nh=128, dc=512, dh=128, dr=64)
+
+
+def test_absorbed_query_projection_at_deepseek_widths():
+    """q_abs_i = W_qabs_i x and q^R_i = RoPE(W^QR_i x) for 32 tokens with the
+    query latent of 1536 ([LLMsBlog] "Query Key Absorption"): W_qabs holds
+    128 x 512 x 1536 fp32 weights (403 MB), streamed once."""
+    m = H.lib()
+    T, din, nh, dc, dr = DS["T"], DS["d_in"], DS["nh"], DS["dc"], DS["dr"]
+    H.say(f"case absorb_query DeepSeek T={T} d_in={din} n_h={nh}")
+    rng = np.random.default_rng(31)
+    W_qabs = (rng.standard_normal((nh, dc, din), dtype=np.float32) * 0.02)
+    W_QR = (rng.standard_normal((nh * dr, din), dtype=np.float32) * 0.02)
+    x = rng.standard_normal((T, din), dtype=np.float32)
+    pos = rng.integers(0, 32768, T).astype(np.int32)
+    qa = torch.empty((T, nh, dc), dtype=torch.float32, device="cuda")
+    qr = torch.empty((T, nh, dr), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_absorb_query_workspace_size(T, din, nh, dc, dr), dtype=torch.uint8, device="cuda")
+    m.mla_absorb_query(_t(x), T, din, _t(W_qabs), _t(W_QR), nh, dc, dr, 10000.0,
+                       torch.from_numpy(pos).cuda(), m.MLA_FP32, qa, qr, ws)
+    torch.cuda.synchronize()
+    ra, rr = oracle.absorb_query(W_qabs, W_QR, x, pos, 10000.0)
+    ea, er = _rel(qa.cpu().numpy(), ra), _rel(qr.cpu().numpy(), rr)
+    H.say(f"  q_abs rel {ea:.2e}, q_rope rel {er:.2e}")
+    assert ea < 1e-5 and er < 1e-5
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_output_projection_at_deepseek_widths(mode):
+    """out = W_ov concat_i(o_i) (merged: 5120 x 65536 fp32 = 1.34 GB of
+    weights) or W^O concat_i(W^UV_i o_i) (two-stage) for 32 tokens ([Zhang]
+    "Value absorption: weight and sum first, project after")."""
+    m = H.lib()
+    T, d, nh, dc, dh = DS["T"], DS["d"], DS["nh"], DS["dc"], DS["dh"]
+    H.say(f"case output_proj DeepSeek mode={mode} T={T} d={d}")
+    rng = np.random.default_rng(32 + mode)
+    o = rng.standard_normal((T, nh, dc), dtype=np.float32) * 0.05
+    if mode == 0:
+        W_ov = rng.standard_normal((d, nh * dc), dtype=np.float32) * 0.02
+        ref = oracle.output_projection_merged(o, W_ov)
+        W1, W2 = _t(W_ov), None
+    else:
+        W_UV = rng.standard_normal((nh * dh, dc), dtype=np.float32) * 0.02
+        W_O = rng.standard_normal((d, nh * dh), dtype=np.float32) * 0.02
+        ref = oracle.output_projection_two_stage(o, W_UV, W_O, nh, dh)
+        W1, W2 = _t(W_UV), _t(W_O)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    wp = torch.empty(m.mla_output_proj_workspace_size(T, nh, dc, dh, d, mode), dtype=torch.uint8,
+                     device="cuda")
+    m.mla_output_proj(_t(o), m.MLA_FP32, T, nh, dc, dh, d, mode, W1, W2, out, wp)
+    torch.cuda.synchronize()
+    e = _rel(out.cpu().numpy(), ref)
+    H.say(f"  rel {e:.2e}")
+    assert e < 1e-5
+
+
+def test_cache_append_at_deepseek_widths():
+    """c = W^DKV h and k^R = RoPE(W^KR h) for 32 tokens of d 5120 ([Mishra]
+    "Step 1: a low-rank latent"), stored in an fp32 cache."""
+    m = H.lib()
+    T, d, dc, dr = DS["T"], DS["d"], DS["dc"], DS["dr"]
+    H.say(f"case cache_append DeepSeek T={T} d={d}")
+    rng = np.random.default_rng(34)
+    h = rng.standard_normal((T, d), dtype=np.float32)
+    W_DKV = rng.standard_normal((dc, d), dtype=np.float32) * 0.02
+    W_KR = rng.standard_normal((dr, d), dtype=np.float32) * 0.02
+    pos = rng.integers(0, 32768, T).astype(np.int32)
+    slots = np.arange(T, dtype=np.int32)[::-1].copy()       # rows land in reverse order
+    cache = torch.zeros((1, 64, dc + dr), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_cache_append_workspace_size(T, d, dc, dr), dtype=torch.uint8, device="cuda")
+    m.mla_cache_append(_t(h), T, d, _t(W_DKV), _t(W_KR), dc, dr, 10000.0,
+                       torch.from_numpy(pos).cuda(), torch.from_numpy(slots).cuda(), m.MLA_FP32,
+                       cache, None, ws)
+    torch.cuda.synchronize()
+    c, kR = oracle.cache_append(W_DKV, W_KR, h, pos, 10000.0)
+    g = cache.cpu().numpy()[0]
+    ec, ek = _rel(g[slots, :dc], c), _rel(g[slots, dc:], kR)
+    H.say(f"  c rel {ec:.2e}, k^R rel {ek:.2e}")
+    assert ec < 1e-5 and ek < 1e-5
