@@ -328,14 +328,29 @@ bool skinny_ok(const GemmArgs& g) {
 
 }  // namespace
 
+// Split count of the skinny GEMM. Three workgroups fit on a CU (their LDS
+// tiles take 42 KB each), so the grid runs in rounds of 3 * 256 workgroups;
+// the split count is the one (of at most 64, with at least 128 k per split)
+// that fills its last round best, the smallest such: a grid of 1.33 rounds
+// would leave two thirds of the chip idle in its second round.
 int skinny_splits(int batch, int M, int N, int K) {
   const int64_t base = static_cast<int64_t>(batch) * ((M + kSM - 1) / kSM) * ((N + kSN - 1) / kSN);
-  int64_t s = (4 * kNumCUs + base - 1) / base;
-  const int64_t kmax = (K + 255) / 256;   // at least 256 k per split
-  if (s > kmax) s = kmax;
-  if (s < 1) s = 1;
-  if (s > 64) s = 64;
-  return static_cast<int>(s);
+  constexpr int64_t kRound = 3LL * kNumCUs;
+  int64_t smax = (K + 127) / 128;   // at least 128 k per split
+  if (smax > 64) smax = 64;
+  if (smax < 1) smax = 1;
+  int64_t best = 1;
+  double best_fill = -1.0;
+  for (int64_t s = 1; s <= smax; ++s) {
+    const int64_t wg = base * s;
+    const int64_t rounds = (wg + kRound - 1) / kRound;
+    const double fill = static_cast<double>(wg) / static_cast<double>(rounds * kRound);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = s;
+    }
+  }
+  return static_cast<int>(best);
 }
 
 size_t gemm_partial_bytes(int batch, int M, int N, int K) {
