@@ -18,6 +18,8 @@
 // step's MFMAs. Rows past M or N and K steps past the end load zeros.
 // Split-K (for skinny M, where the output tiles alone do not fill the chip)
 // writes fp32 partial tiles that a second kernel sums in split order.
+#include <type_traits>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -123,6 +125,196 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
       }
 }
 
+// ---- large-tile variant: 256 x 256 output tile, one wavefront per SIMD ----
+// Workgroup = 4 wavefronts in 2 x 2, each 128 x 128 as 4 x 4
+// v_mfma_f32_32x32x16_bf16 tiles (its 256 accumulation registers): every
+// 16-byte fragment read from LDS feeds four MFMAs, against two in the 128 x 128
+// tile. K advances 32 at a time through a ring of four 32 KB LDS stages
+// (A 256 x 32 and B 256 x 32 bf16) filled straight from memory with
+// global_load_lds_dwordx4 (no register round trip), three stages ahead, so
+// that about three stages of matrix work cover the memory latency. A stage
+// row is 64 bytes; 16-byte unit u of row r sits at position u ^ ((r >> 2) & 3),
+// which puts the fragment reads of 16 consecutive rows in distinct bank
+// groups. Rows past M or N are read from row M - 1 or N - 1 and their outputs
+// are not stored; the k range of a split must be a multiple of 32.
+constexpr int kLM = 256, kLN = 256, kLK = 32, kLS = 4;
+#ifndef MLA_GEMM_BIG_MIN_TILES
+#define MLA_GEMM_BIG_MIN_TILES 240   // smallest grid (tiles x splits) the large tile takes
+#endif
+#ifndef MLA_GEMM_BIG_MIN_K
+#define MLA_GEMM_BIG_MIN_K 1024      // smallest k range per split it takes
+#endif
+constexpr int kLStage = (kLM + kLN) * kLK * 2;   // 32 KB
+constexpr int kLCopies = 8;                      // copy instructions per wavefront and stage
+
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding)
+#define GEMM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+// f(integral_constant<int, I>) for I = 0 .. 3, unrolled at compile time
+template <class F>
+__device__ __forceinline__ void static_for4(F&& f) {
+  f(std::integral_constant<int, 0>{});
+  f(std::integral_constant<int, 1>{});
+  f(std::integral_constant<int, 2>{});
+  f(std::integral_constant<int, 3>{});
+}
+
+// Tile order: workgroup ids congruent mod 8 run on one XCD (the dispatcher
+// deals them out in turn), so XCD x is given the x-th contiguous eighth of the
+// tiles in a grouped order: groups of kLGroup tile rows, each walked column by
+// column. The tiles one XCD runs at a time then share a few A row blocks and
+// B column blocks, which its L2 serves after the first read, instead of every
+// tile fetching its own from memory.
+#ifndef MLA_GEMM_GROUP
+#define MLA_GEMM_GROUP 4
+#endif
+constexpr int kLGroup = MLA_GEMM_GROUP;
+
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, int k_per_split,
+                                                               int tiles_m, int tiles_n, int tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLS * kLStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int per = (tiles + 7) / 8;
+  const int t = static_cast<int>(blockIdx.x % 8) * per + static_cast<int>(blockIdx.x / 8);
+  if (t >= tiles) return;
+  const int mn = tiles_m * tiles_n;
+  // (the divisions run on the vector unit: readfirstlane keeps the results
+  // scalar, as the copy addresses need)
+  const int kz = __builtin_amdgcn_readfirstlane(t / mn), rt = t % mn;
+  const int grp = rt / (kLGroup * tiles_n), rr = rt % (kLGroup * tiles_n);
+  const int gsz = min(kLGroup, tiles_m - grp * kLGroup);
+  const int64_t m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(grp * kLGroup + rr % gsz)) * kLM;
+  const int64_t n0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(rr / gsz)) * kLN;
+  const int kb = kz * k_per_split;
+  const int ke = min(g.K, kb + k_per_split);
+  const int nst = ke > kb ? (ke - kb) / kLK : 0;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)smem));
+
+  // copies: wavefronts 0 and 1 fill rows 128 w .. of the A tile, 2 and 3 rows
+  // 128 (w - 2) .. of the B tile; instruction j covers 16 rows: lane i reads
+  // row 16 j + i / 4, logical unit (i & 3) ^ ((i >> 4) & 3), and lands at
+  // byte 1024 j + 16 i of the wavefront's 8 KB
+  const bool isA = w < 2;
+  const uint8_t* mat = reinterpret_cast<const uint8_t*>(isA ? g.A : g.B);
+  const int64_t ld = isA ? g.lda : g.ldb;
+  const int64_t lim = (isA ? g.M : g.N) - 1;
+  const int64_t r0 = (isA ? m0 : n0) + 128 * (w & 1);
+  const uint32_t dst0 = (isA ? 0u : static_cast<uint32_t>(kLM * kLK * 2)) + 8192u * (w & 1);
+  uint32_t voff[kLCopies];
+#pragma unroll
+  for (int j = 0; j < kLCopies; ++j) {
+    int64_t row = r0 + 16 * j + (lane >> 2);
+    row = row < lim ? row : lim;
+    voff[j] = static_cast<uint32_t>(row * ld * 2) + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+  }
+  auto issue = [&](int st) {
+    const uint8_t* src = mat + 2LL * (kb + kLK * st);
+    asm volatile("" : "+s"(src));
+    const uint32_t dst = lds0 + (st % kLS) * kLStage + dst0;
+#pragma unroll
+    for (int j = 0; j < kLCopies; ++j) dma16(src, voff[j], dst + 1024 * j);
+  };
+
+  // fragment reads: row r of a tile, unit 2 kk + half, at r * 64 +
+  // 16 ((2 kk + half) ^ ((r >> 2) & 3)); (r >> 2) & 3 = (l32 >> 2) & 3
+  const uint32_t sw = (l32 >> 2) & 3;
+  const uint32_t fa = l32 * 64u + 16u * (static_cast<uint32_t>(half) ^ sw);          // kk = 0
+  const uint32_t fb = l32 * 64u + 16u * (static_cast<uint32_t>(2 + half) ^ sw);      // kk = 1
+  auto frag = [&](uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(static_cast<uintptr_t>(a));
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+  const int pre = nst < kLS - 1 ? nst : kLS - 1;
+  for (int st = 0; st < pre; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    // stage st has landed when at most the copies of the stages issued after
+    // it (up to two) are still in flight
+    const int later = min(nst - 1 - st, kLS - 2);
+    if (later >= 2) GEMM_WAIT_VM(2 * kLCopies);
+    else if (later == 1) GEMM_WAIT_VM(kLCopies);
+    else GEMM_WAIT_VM(0);
+    // every wavefront's copies of stage st are visible, and every wavefront
+    // is done with stage st - 1, whose buffer the next copy refills
+    __syncthreads();
+    // the copies of stage st + 3 go out one per four MFMAs below: issued all
+    // at once they would stall the wavefront on the memory queue
+    const bool cp = st + kLS - 1 < nst;
+    const uint8_t* csrc = mat + 2LL * (kb + kLK * (st + kLS - 1));
+    asm volatile("" : "+s"(csrc));
+    const uint32_t cdst = lds0 + ((st + kLS - 1) % kLS) * kLStage + dst0;
+    const uint32_t sb = lds0 + (st % kLS) * kLStage;
+    const uint32_t sa = sb + wm * 128 * 64, sbb = sb + kLM * kLK * 2 + wn * 128 * 64;
+    // all 16 fragments of the stage are read before its first MFMA (the
+    // scheduling barrier keeps the compiler from trading them for registers
+    // by reloading one fragment per group of MFMAs, which would expose the LDS
+    // latency four times per k step)
+    bf16x8_t a[2][4], b[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[kk][i] = frag(sa + i * 32 * 64 + (kk ? fb : fa));
+        b[kk][i] = frag(sbb + i * 32 * 64 + (kk ? fb : fa));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+        if (cp) dma16(csrc, voff[4 * kk + i], cdst + 1024 * (4 * kk + i));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+
+  // acc[i][j] register r holds C[m][n] with m = 8 (r / 4) + 4 half + r % 4 and
+  // n = l32 within the 32 x 32 tile (i, j) of the wavefront's 128 x 128 block
+  const int64_t mw = m0 + wm * 128 + 4 * half, nw = n0 + wn * 128 + l32;
+  // one pass per output form, the bounds tests only on edge tiles
+  auto store_all = [&](auto put) {
+    const bool edge = m0 + kLM > g.M || n0 + kLN > g.N;
+    static_for4([&](auto I) {
+      static_for4([&](auto J) {
+        constexpr int i = decltype(I)::value, j = decltype(J)::value;
+        const int64_t n = nw + j * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = mw + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (!edge || (m < g.M && n < g.N)) put(m, n, acc[i][j][r]);
+        }
+        // one tile's stores at a time (the addresses of all 256 would not
+        // fit the registers)
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
+  if (g.splits > 1) {
+    float* part = g.partial + static_cast<int64_t>(kz) * g.M * g.N;
+    store_all([&](int64_t m, int64_t n, float v) { part[m * g.N + n] = v; });
+  } else if (g.c_bf16) {
+    uint16_t* c = static_cast<uint16_t*>(g.C);
+    store_all([&](int64_t m, int64_t n, float v) { c[m * g.ldc + n] = f32_to_bf16(v); });
+  } else {
+    float* c = static_cast<float*>(g.C);
+    store_all([&](int64_t m, int64_t n, float v) { c[m * g.ldc + n] = v; });
+  }
+}
+
 // C = sum over the splits of the fp32 partial tiles, in split order.
 __global__ __launch_bounds__(256) void gemm_split_reduce(MfmaGemmArgs g) {
   const int64_t total = static_cast<int64_t>(g.M) * g.N;
@@ -154,9 +346,26 @@ mla_status launch_gemm_bf16(const MfmaGemmArgs& g, hipStream_t st) {
   a.splits = gz;
   if (gz > 1 && a.partial == nullptr)
     return fail(MLA_ERR_INVALID_ARGUMENT, "bf16 GEMM: split-K needs a partial buffer");
-  const dim3 grid(static_cast<unsigned>((g.N + kBN - 1) / kBN), static_cast<unsigned>((g.M + kBM - 1) / kBM),
-                  static_cast<unsigned>(gz));
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, a, kps);
+  // the large tile where its grid still covers the chip, each split runs
+  // long enough (at least 1024 k) to repay its deeper pipeline, K is a
+  // multiple of its k step and the per-lane 32-bit copy offsets reach every
+  // row (measured on the prefill projections: 0.54 -> 0.38 ms at 4096 x 24576
+  // x 1536, 0.97 -> 0.92 ms at 4096 x 5120 x 16384; shorter k ranges and
+  // grids below the chip run faster on the 128 x 128 tile)
+  const int64_t big_tiles = static_cast<int64_t>((g.N + kLN - 1) / kLN) * ((g.M + kLM - 1) / kLM) * gz;
+  const bool big = g.K % kLK == 0 && big_tiles >= MLA_GEMM_BIG_MIN_TILES && kps >= MLA_GEMM_BIG_MIN_K &&
+                   static_cast<int64_t>(g.M) * g.lda * 2 < (1LL << 32) &&
+                   static_cast<int64_t>(g.N) * g.ldb * 2 < (1LL << 32);
+  if (big) {
+    const int tm = (g.M + kLM - 1) / kLM, tn = (g.N + kLN - 1) / kLN;
+    const int tiles = tm * tn * gz;
+    const unsigned blocks = static_cast<unsigned>((tiles + 7) / 8 * 8);
+    hipLaunchKernelGGL(gemm_bf16_big_kernel, dim3(blocks), dim3(256), 0, st, a, kps, tm, tn, tiles);
+  } else {
+    const dim3 grid(static_cast<unsigned>((g.N + kBN - 1) / kBN), static_cast<unsigned>((g.M + kBM - 1) / kBM),
+                    static_cast<unsigned>(gz));
+    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, a, kps);
+  }
   if (gz > 1) {
     const int64_t total = static_cast<int64_t>(g.M) * g.N;
     const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
