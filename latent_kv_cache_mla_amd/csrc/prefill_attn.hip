@@ -62,10 +62,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int b = blockIdx.z, head = blockIdx.y;
-  // heavy (late) query tiles first
+  // heads vary fastest, then the query tile from the last (the heaviest: it
+  // sees the most keys) to the first: the dispatcher starts every head's
+  // heaviest tile before any lighter one, which keeps the tail of the grid
+  // short (longest work first)
+  const int b = blockIdx.z, head = blockIdx.x;
   const int n_qt = (a.max_seq_len + kQT - 1) / kQT;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x);
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.y);
   const int s0 = a.cu_seqlens[b], S = a.cu_seqlens[b + 1] - s0;
   const int q0 = qt * kQT;
   if (q0 >= S) return;
@@ -237,7 +240,7 @@ bool prefill_attn_supported(int d_h, int d_rope, int d_v) {
 }
 
 mla_status launch_prefill_attn(const PrefillAttnArgs& a, int d_h, int d_rope, int d_v, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((a.max_seq_len + kQT - 1) / kQT), static_cast<unsigned>(a.n_heads),
+  const dim3 grid(static_cast<unsigned>(a.n_heads), static_cast<unsigned>((a.max_seq_len + kQT - 1) / kQT),
                   static_cast<unsigned>(a.batch));
   if (d_h == 128 && d_rope == 64 && d_v == 128)
     hipLaunchKernelGGL((prefill_attn_kernel<128, 64, 128>), grid, dim3(256), 0, st, a);
