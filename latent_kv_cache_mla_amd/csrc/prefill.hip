@@ -71,9 +71,71 @@ __global__ __launch_bounds__(256) void rope_round_kernel(float* __restrict__ X, 
   }
 }
 
+// The same pass, one workgroup per row, 8 columns per thread and step (two
+// 16-byte loads, one 16-byte store): the row's d_r / 2 angles are computed
+// once into LDS (fp64, as above), then every 8-column unit is either rounded
+// or, inside a rope block, rotated (4 pairs) and rounded. Needs X and Y rows
+// 16-byte aligned, width a multiple of 8 and, with rope blocks, r0 and d_r
+// multiples of 8 and d_r at most 256.
+__global__ __launch_bounds__(256) void rope_round8_kernel(float* __restrict__ X, int64_t ldx, int width,
+                                                          int r0, int n_rope, int d_r,
+                                                          const int32_t* __restrict__ positions,
+                                                          double theta, uint16_t* __restrict__ Y,
+                                                          int64_t ldy, int write_back) {
+  __shared__ float cs_lds[128], sn_lds[128];
+  const int64_t t = blockIdx.x;
+  const int half_r = d_r / 2;
+  if (n_rope > 0) {
+    if (threadIdx.x < half_r) {
+      float c, sn;
+      rope_cs(positions[t], static_cast<int>(threadIdx.x), d_r, theta, &c, &sn);
+      cs_lds[threadIdx.x] = c;
+      sn_lds[threadIdx.x] = sn;
+    }
+    __syncthreads();
+  }
+  float* x = X + t * ldx;
+  uint16_t* y = Y + t * ldy;
+  const int rope_end = r0 + n_rope * d_r;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  for (int col = 8 * static_cast<int>(threadIdx.x); col < width; col += 8 * 256) {
+    f4 v0 = *reinterpret_cast<const f4*>(x + col);
+    f4 v1 = *reinterpret_cast<const f4*>(x + col + 4);
+    float e[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    if (col >= r0 && col < rope_end) {
+      const int k0 = ((col - r0) % d_r) / 2;   // first pair of the unit
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float c = cs_lds[k0 + p], sn = sn_lds[k0 + p];
+        const float a = e[2 * p], b = e[2 * p + 1];
+        e[2 * p] = a * c - b * sn;
+        e[2 * p + 1] = a * sn + b * c;
+      }
+      if (write_back) {
+        *reinterpret_cast<f4*>(x + col) = f4{e[0], e[1], e[2], e[3]};
+        *reinterpret_cast<f4*>(x + col + 4) = f4{e[4], e[5], e[6], e[7]};
+      }
+    }
+    u4 o;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      o[p] = static_cast<uint32_t>(f32_to_bf16(e[2 * p])) | (static_cast<uint32_t>(f32_to_bf16(e[2 * p + 1])) << 16);
+    *reinterpret_cast<u4*>(y + col) = o;
+  }
+}
+
 mla_status launch_rope_round(float* X, int64_t ldx, int width, int r0, int n_rope, int d_r,
                              const int32_t* positions, float theta, uint16_t* Y, int64_t ldy,
                              int write_back, int64_t T, hipStream_t st) {
+  if (T > 0 && T < 0x7FFFFFFF && aligned16(X) && aligned16(Y) && ldx % 4 == 0 && ldy % 8 == 0 &&
+      width % 8 == 0 && (n_rope == 0 || (r0 % 8 == 0 && d_r % 8 == 0 && d_r <= 256))) {
+    hipLaunchKernelGGL(rope_round8_kernel, dim3(static_cast<unsigned>(T)), dim3(256), 0, st, X, ldx, width, r0,
+                       n_rope, d_r, positions, static_cast<double>(theta), Y, ldy, write_back);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "rope launch: %s", hipGetErrorString(e));
+    return MLA_OK;
+  }
   const int64_t work = T * (width > d_r / 2 ? width : d_r / 2);
   const unsigned blocks = static_cast<unsigned>((work + 255) / 256 < 8192 ? (work + 255) / 256 : 8192);
   hipLaunchKernelGGL(rope_round_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, X, ldx, width, r0,
