@@ -289,11 +289,11 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
   uint16_t* ob = reinterpret_cast<uint16_t*>(ws + L.ob);
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   auto gemm = [&](int M, int N, int K, const uint16_t* A, int64_t lda, const void* B, int64_t ldb,
-                  void* C, int64_t ldc, int c_bf16) {
+                  void* C, int64_t ldc, int c_bf16, int splits = 1, float* partial = nullptr) {
     MfmaGemmArgs g{};
     g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda;
     g.B = static_cast<const uint16_t*>(B); g.ldb = ldb;
-    g.C = C; g.ldc = ldc; g.c_bf16 = c_bf16; g.splits = 1; g.partial = nullptr;
+    g.C = C; g.ldc = ldc; g.c_bf16 = c_bf16; g.splits = splits; g.partial = partial;
     return launch_gemm_bf16(g, st);
   };
   const int LW = dc + dr;   // latent row width
@@ -325,9 +325,24 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
                             krb, dr > 0 ? dr : 8, kv + static_cast<int64_t>(nh) * dh, 2 * nh * dh,
                             cu_seqlens, scale, ob, static_cast<int64_t>(nh) * dh, lse, stream);
   if (s != MLA_OK) return s;
-  // 6. out = W^O [o_1 ; ... ; o_{n_h}]
-  return gemm(T32, D, nh * dh, ob, static_cast<int64_t>(nh) * dh, w->W_O, static_cast<int64_t>(nh) * dh,
-              out, D, 0);
+  // 6. out = W^O [o_1 ; ... ; o_{n_h}], with K split into up to four parts
+  // when that fills the last round of 256 workgroups better (320 tiles of
+  // 256 x 256 at 4096 tokens and d 5120 are 1.25 rounds; four splits make five
+  // full ones). The fp32 partial tiles go to the q32 region, which nothing
+  // reads once the attention has run.
+  const int KO = nh * dh;
+  const int64_t tiles = static_cast<int64_t>((T32 + 255) / 256) * ((D + 255) / 256);
+  int so = 1;
+  double best = static_cast<double>((tiles + 255) / 256);
+  for (int sp = 2; sp <= 4; ++sp) {
+    const int kps = gemm_bf16_k_per_split(KO, sp);
+    const int gz = (KO + kps - 1) / kps;
+    const size_t need = sizeof(float) * static_cast<size_t>(gz) * static_cast<size_t>(T) * D;
+    if (kps < 1024 || need > L.qb - L.q32) break;
+    const double cost = static_cast<double>((tiles * gz + 255) / 256) / gz;
+    if (cost < best - 1e-9) { best = cost; so = sp; }
+  }
+  return gemm(T32, D, KO, ob, KO, w->W_O, KO, out, D, 0, so, so > 1 ? q32 : nullptr);
 }
 
 }  // extern "C"
