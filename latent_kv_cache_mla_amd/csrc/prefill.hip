@@ -297,8 +297,24 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
     return launch_gemm_bf16(g, st);
   };
   const int LW = dc + dr;   // latent row width
-  // 1. the latent row [c ; k^R] (fp32), k^R rotated in place; bf16 copies
-  if ((s = gemm(T32, LW, D, hb, D, w->W_DKVR, D, lat, LW, 0)) != MLA_OK) return s;
+  // 1. the latent row [c ; k^R] (fp32), k^R rotated in place; bf16 copies.
+  // Its few output columns give few 128 x 128 tiles (160 at 4096 tokens and
+  // a 576-wide latent, a third of one round of the chip's 512 workgroup
+  // slots), so K is split (up to four parts) while the grid stays within one
+  // round; the partial tiles go to the q32 region, not yet written.
+  {
+    const int64_t tiles = static_cast<int64_t>((T32 + 127) / 128) * ((LW + 127) / 128);
+    int sl = 1;
+    for (int sp = 2; sp <= 4; ++sp) {
+      const int kps = gemm_bf16_k_per_split(D, sp);
+      const int gz = (D + kps - 1) / kps;
+      const size_t need = sizeof(float) * static_cast<size_t>(gz) * static_cast<size_t>(T) * LW;
+      if (kps < 256 || tiles * gz > 2 * kNumCUs || need > L.qb - L.q32) break;
+      sl = sp;
+    }
+    if ((s = gemm(T32, LW, D, hb, D, w->W_DKVR, D, lat, LW, 0, sl, sl > 1 ? q32 : nullptr)) != MLA_OK)
+      return s;
+  }
   if ((s = launch_rope_round(lat, LW, dc, 0, 0, 2, positions, d->rope_theta, cb, dc, 0, T, st)) != MLA_OK)
     return s;
   if (dr > 0 && (s = launch_rope_round(lat + dc, LW, dr, 0, 1, dr, positions, d->rope_theta, krb, dr, 1, T,
