@@ -175,7 +175,9 @@ def _positions_to_check(pcfg):
         if pcfg.name == "prefill-tiny":
             ts = list(range(S))
         elif pcfg.name == "prefill-ds":
-            ts = [0, 1, 63, 64, 200, 333]
+            # early positions, and the last of each quarter: the last is in the
+            # heaviest query tile and sees every key
+            ts = [0, 1, 63, 64, 200, 333, 1023, 2047, 4095]
         else:
             ts = sorted({0, 1, 31, 32, 127, 128, S - 1} | set(rng.integers(0, S, 3).tolist()))
         picks += [(b, int(cu[b]), t) for t in ts if t < S]
