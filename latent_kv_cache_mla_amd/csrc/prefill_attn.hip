@@ -29,6 +29,8 @@
 // LDS rows are padded (keys: 16 bytes, values: 32 bytes) so that the 16-byte
 // key-fragment reads and the transposed value reads are free of bank
 // conflicts.
+#include <algorithm>
+
 #include "internal.h"
 #include "device_common.h"
 
@@ -38,6 +40,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQT = 128;   // query positions per workgroup
 constexpr int kKT = 32;    // key positions per LDS tile
@@ -55,9 +58,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   constexpr int PV = DV + 16;    // value row pitch (elements)
   constexpr int KTILE = kKT * PK, VTILE = kKT * PV;
   constexpr int CK = DC / 8, CR = DR / 8, CV = DV / 8;   // 16-byte chunks per row part
-  constexpr int CROW = CK + CR + CV;
-  constexpr int NCH = kKT * CROW;                        // chunks per tile
-  constexpr int NLD = (NCH + 255) / 256;                 // per thread
+  // loads of a tile: each instruction covers one part (content keys, rope
+  // keys, values); part p's 32 CP chunks take ceil(32 CP / 256) instructions
+  constexpr int NK = (kKT * CK + 255) / 256, NR = (kKT * CR + 255) / 256, NV = (kKT * CV + 255) / 256;
+  constexpr int NLD = NK + NR + NV;
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][KTILE + VTILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -92,39 +96,69 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     }
   }
 
-  // ---- tile loads: chunk c of a tile is (row c / CROW, part of the row)
-  uint4 st[NLD];
-  auto gload = [&](int kt) {
+  const uint32_t lds0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&kv_lds[0][0]));
+
+  // ---- tile loads. Instruction j of part p: thread tid takes chunk
+  // c = tid + 256 (j - first instruction of p), row c / CP, 16-byte chunk
+  // c % CP of the part's row. Its byte offsets from the part's first row of
+  // the tile (global) and in the LDS tile are the same for every tile, so
+  // they are formed once; per tile only the three row pointers move, and
+  // only a tile that crosses the sequence end tests rows.
+  auto part_of = [](int j) { return j < NK ? 0 : (j < NK + NR ? 1 : 2); };
+  auto chunks_of = [](int p) { return p == 0 ? CK : (p == 1 ? CR : CV); };
+  auto first_of = [](int p) { return p == 0 ? 0 : (p == 1 ? NK : NK + NR); };
+  uint32_t goff[NLD], loff[NLD];
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int c = tid + 256 * j;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < NCH) {
-        const int row = c / CROW, x = c % CROW;
-        const int key = kt * kKT + row;
-        if (key < S) {
-          const int64_t t = s0 + key;
-          const uint16_t* src;
-          if (x < CK) src = a.k + t * a.ldk + static_cast<int64_t>(head) * DC + 8 * x;
-          else if (x < CK + CR) src = a.kr + t * a.ldkr + 8 * (x - CK);
-          else src = a.v + t * a.ldv + static_cast<int64_t>(head) * DV + 8 * (x - CK - CR);
-          v = *reinterpret_cast<const uint4*>(src);
-        }
+  for (int j = 0; j < NLD; ++j) {
+    const int p = part_of(j), cp = chunks_of(p);
+    const int c = tid + 256 * (j - first_of(p));
+    const int row = min(c / cp, kKT - 1), x = c % cp;
+    const int64_t ld = p == 0 ? a.ldk : (p == 1 ? a.ldkr : a.ldv);
+    goff[j] = static_cast<uint32_t>(row * ld * 2 + 16 * x);
+    loff[j] = p == 0   ? static_cast<uint32_t>(row * PK * 2 + 16 * x)
+              : p == 1 ? static_cast<uint32_t>(row * PK * 2 + 2 * DC + 16 * x)
+                       : static_cast<uint32_t>(KTILE * 2 + row * PV * 2 + 16 * x);
+  }
+  // whether thread tid holds a chunk in instruction j (false only in a
+  // part's last instruction, and then for whole wavefronts: 32 CP is a
+  // multiple of 64)
+  auto active = [&](int j) {
+    const int p = part_of(j);
+    return kKT * chunks_of(p) % 256 == 0 || tid + 256 * (j - first_of(p)) < kKT * chunks_of(p);
+  };
+  u32x4_t st[NLD];
+  auto gload = [&](int kt) {
+    const int64_t t0 = s0 + static_cast<int64_t>(kt) * kKT;
+    const uint8_t* base[3] = {
+        reinterpret_cast<const uint8_t*>(a.k + t0 * a.ldk + static_cast<int64_t>(head) * DC),
+        reinterpret_cast<const uint8_t*>(a.kr + t0 * a.ldkr),
+        reinterpret_cast<const uint8_t*>(a.v + t0 * a.ldv + static_cast<int64_t>(head) * DV)};
+    const int lim = S - 1 - kt * kKT;   // the tile's last row inside the sequence
+    if (lim >= kKT - 1) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        st[j] = active(j) ? *reinterpret_cast<const u32x4_t*>(base[part_of(j)] + goff[j]) : u32x4_t{};
+    } else {
+      // the tile crosses the sequence end: rows past it read the last row
+      // (their scores are masked, so their weights are exactly zero)
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int p = part_of(j), cp = chunks_of(p);
+        const int c = tid + 256 * (j - first_of(p));
+        const int64_t ld = p == 0 ? a.ldk : (p == 1 ? a.ldkr : a.ldv);
+        const int64_t off = static_cast<int64_t>(min(c / cp, lim)) * ld * 2 + 16 * (c % cp);
+        st[j] = active(j) ? *reinterpret_cast<const u32x4_t*>(base[p] + off) : u32x4_t{};
       }
-      st[j] = v;
     }
   };
   auto swrite = [&](int buf) {
+    const uint32_t tb = static_cast<uint32_t>(buf) * ((KTILE + VTILE) * 2);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int c = tid + 256 * j;
-      if (c < NCH) {
-        const int row = c / CROW, x = c % CROW;
-        uint16_t* dst = x < CK + CR ? &kv_lds[buf][row * PK + 8 * x]
-                                    : &kv_lds[buf][KTILE + row * PV + 8 * (x - CK - CR)];
-        *reinterpret_cast<uint4*>(dst) = st[j];
-      }
-    }
+    for (int j = 0; j < NLD; ++j)
+      if (active(j))
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+            static_cast<uintptr_t>(lds0 + tb + loff[j])) = st[j];
   };
 
   f32x16_t o[DV / 32];
@@ -134,8 +168,6 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   const float c = a.c_log2;
 
   // LDS byte addresses of this lane's fragments within a tile
-  const uint32_t lds0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&kv_lds[0][0]));
   const uint32_t tile_bytes = (KTILE + VTILE) * 2;
   const uint32_t k_off = (l32 * PK + 8 * half) * 2;
   // transposed value reads: 16-lane group g16, source lane s16 supplies key
@@ -240,6 +272,11 @@ bool prefill_attn_supported(int d_h, int d_rope, int d_v) {
 }
 
 mla_status launch_prefill_attn(const PrefillAttnArgs& a, int d_h, int d_rope, int d_v, hipStream_t st) {
+  // the per-lane byte offsets of a tile's rows are 32-bit
+  const int64_t ld_max = std::max(a.ldk, std::max(a.ldkr, a.ldv));
+  if (ld_max < 0 || ld_max * 2 * kKT >= (int64_t{1} << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "prefill attention: key/value row stride %lld too large",
+                static_cast<long long>(ld_max));
   const dim3 grid(static_cast<unsigned>(a.n_heads), static_cast<unsigned>((a.max_seq_len + kQT - 1) / kQT),
                   static_cast<unsigned>(a.batch));
   if (d_h == 128 && d_rope == 64 && d_v == 128)
