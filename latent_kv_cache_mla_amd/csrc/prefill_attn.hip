@@ -26,7 +26,7 @@
 //   * O^T [d_v x 32 queries] += V^T P^T: P^T straight from the score
 //     registers (bf16), V^T read from the row-major value tile with the LDS
 //     transpose load in the key order that matches the score registers.
-// LDS rows are padded (keys: 16 bytes, values: 32 bytes) so that the 16-byte
+// LDS rows are padded (keys: 16 bytes, values: 64 bytes) so that the 16-byte
 // key-fragment reads and the transposed value reads are free of bank
 // conflicts.
 #include <algorithm>
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   constexpr int DQK = DC + DR;
   static_assert(DQK % 16 == 0 && DC % 8 == 0 && DR % 8 == 0 && DV % 32 == 0, "head dims");
   constexpr int PK = DQK + 8;    // key row pitch (elements)
-  constexpr int PV = DV + 16;    // value row pitch (elements)
+  constexpr int PV = DV + 32;    // value row pitch (elements)
   constexpr int KTILE = kKT * PK, VTILE = kKT * PV;
   constexpr int CK = DC / 8, CR = DR / 8, CV = DV / 8;   // 16-byte chunks per row part
   // loads of a tile: each instruction covers one part (content keys, rope
@@ -186,13 +186,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
     // tiles that start after the wavefront's last query are fully masked
     if (kt * kKT <= w_last) {
       const uint32_t tb = lds0 + buf * tile_bytes;
+      // every key fragment of the tile is read before the first product (the
+      // scheduling barrier keeps the compiler from interleaving the reads
+      // with the products, which would expose the LDS latency at each pair)
+      bf16x8_t kf[DQK / 16];
+#pragma unroll
+      for (int kc = 0; kc < DQK / 16; ++kc)
+        kf[kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            static_cast<uintptr_t>(tb + k_off + 32 * kc));
+      __builtin_amdgcn_sched_barrier(0);
       f32x16_t s = f32x16_t{};
 #pragma unroll
-      for (int kc = 0; kc < DQK / 16; ++kc) {
-        const bf16x8_t kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            static_cast<uintptr_t>(tb + k_off + 32 * kc));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kc], s, 0, 0, 0);
-      }
+      for (int kc = 0; kc < DQK / 16; ++kc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
       // register r holds key kt * 32 + 8 (r / 4) + 4 half + r % 4 of query
       // qrow; only a tile that reaches past the wavefront's first query or the
       // sequence end needs the mask (a wave-uniform test)
