@@ -50,21 +50,50 @@ __device__ __forceinline__ s16x4_t tr16(uint32_t a) {
       (__attribute__((address_space(3))) s16x4_t*)(static_cast<uintptr_t>(a)));
 }
 
+// One part of a key/value tile in LDS (content keys, rope keys or values):
+// 32 rows of CP 16-byte chunks, stored as 1 KB blocks of R = 64 / CP rows,
+// each filled by one direct global-to-LDS copy instruction (lane L writes
+// bytes 16 L .. 16 L + 15 of the block). Within a block the chunks are
+// column-major: chunk x of the block's row rr is at 16 (R x + rr). Blocks
+// are 1024 + 1024 / CP bytes apart (CP >= 8), which shifts each block by a
+// quarter or half of the LDS banks: the key-fragment reads (16 rows, one
+// chunk) and the transposed value reads (4 rows, 4 chunks) then touch
+// every bank once.
+template <int CP>
+struct TileRegion {
+  static constexpr int R = CP > 0 ? 64 / CP : 1;   // rows per block
+  static constexpr int NB = CP > 0 ? 32 / R : 0;   // blocks
+  static constexpr int kStride = 1024 + (CP >= 8 ? 1024 / CP : 0);
+  static constexpr int kBytes = NB * kStride;
+  // byte offset of row r, chunk x
+  static __device__ __forceinline__ constexpr uint32_t at(int r, int x) {
+    return static_cast<uint32_t>((r / R) * kStride + 16 * (R * x + r % R));
+  }
+};
+
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left free (gfx9 encoding)
+#define PA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
 template <int DC, int DR, int DV>
 __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a) {
   constexpr int DQK = DC + DR;
   static_assert(DQK % 16 == 0 && DC % 8 == 0 && DR % 8 == 0 && DV % 32 == 0, "head dims");
-  constexpr int PK = DQK + 8;    // key row pitch (elements)
-  constexpr int PV = DV + 32;    // value row pitch (elements)
-  constexpr int KTILE = kKT * PK, VTILE = kKT * PV;
   constexpr int CK = DC / 8, CR = DR / 8, CV = DV / 8;   // 16-byte chunks per row part
-  // loads of a tile: each instruction covers one part (content keys, rope
-  // keys, values); part p's 32 CP chunks take ceil(32 CP / 256) instructions
-  constexpr int NK = (kKT * CK + 255) / 256, NR = (kKT * CR + 255) / 256, NV = (kKT * CV + 255) / 256;
-  constexpr int NLD = NK + NR + NV;
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][KTILE + VTILE];
+  static_assert(CK == 16 || CK == 8, "content key width");
+  static_assert(CR == 0 || CR == 2 || CR == 4 || CR == 8, "rope key width");
+  static_assert(CV == 16 || CV == 8, "value width");
+  using RK = TileRegion<CK>;
+  using RR = TileRegion<CR>;
+  using RV = TileRegion<CV>;
+  constexpr uint32_t kOffR = RK::kBytes, kOffV = RK::kBytes + RR::kBytes;
+  constexpr uint32_t kTileBytes = RK::kBytes + RR::kBytes + RV::kBytes;
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * kTileBytes];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int half = lane >> 5, l32 = lane & 31;
   // heads vary fastest, then the query tile from the last (the heaviest: it
   // sees the most keys) to the first: the dispatcher starts every head's
@@ -97,68 +126,42 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   }
 
   const uint32_t lds0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&kv_lds[0][0]));
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&kv_lds[0]));
 
-  // ---- tile loads. Instruction j of part p: thread tid takes chunk
-  // c = tid + 256 (j - first instruction of p), row c / CP, 16-byte chunk
-  // c % CP of the part's row. Its byte offsets from the part's first row of
-  // the tile (global) and in the LDS tile are the same for every tile, so
-  // they are formed once; per tile only the three row pointers move, and
-  // only a tile that crosses the sequence end tests rows.
-  auto part_of = [](int j) { return j < NK ? 0 : (j < NK + NR ? 1 : 2); };
-  auto chunks_of = [](int p) { return p == 0 ? CK : (p == 1 ? CR : CV); };
-  auto first_of = [](int p) { return p == 0 ? 0 : (p == 1 ? NK : NK + NR); };
-  uint32_t goff[NLD], loff[NLD];
+  // ---- tile copies, straight from global memory into LDS. Wavefront w
+  // fills blocks w, w + 4, ... of each part; lane L of block b copies row
+  // b R + L % R, chunk L / R. A lane's byte offset from the block's first
+  // row is the same for every block and tile; the row pointers are scalar.
+  const uint32_t gk = static_cast<uint32_t>((lane % RK::R) * a.ldk * 2 + 16 * (lane / RK::R));
+  const uint32_t gr = static_cast<uint32_t>((lane % RR::R) * a.ldkr * 2 + 16 * (lane / RR::R));
+  const uint32_t gv = static_cast<uint32_t>((lane % RV::R) * a.ldv * 2 + 16 * (lane / RV::R));
+  auto copy_part = [&](auto region, const uint16_t* rows, int64_t ld, uint32_t lane_off,
+                       uint32_t dst, int lim) {
+    using RG = decltype(region);
 #pragma unroll
-  for (int j = 0; j < NLD; ++j) {
-    const int p = part_of(j), cp = chunks_of(p);
-    const int c = tid + 256 * (j - first_of(p));
-    const int row = min(c / cp, kKT - 1), x = c % cp;
-    const int64_t ld = p == 0 ? a.ldk : (p == 1 ? a.ldkr : a.ldv);
-    goff[j] = static_cast<uint32_t>(row * ld * 2 + 16 * x);
-    loff[j] = p == 0   ? static_cast<uint32_t>(row * PK * 2 + 16 * x)
-              : p == 1 ? static_cast<uint32_t>(row * PK * 2 + 2 * DC + 16 * x)
-                       : static_cast<uint32_t>(KTILE * 2 + row * PV * 2 + 16 * x);
-  }
-  // whether thread tid holds a chunk in instruction j (false only in a
-  // part's last instruction, and then for whole wavefronts: 32 CP is a
-  // multiple of 64)
-  auto active = [&](int j) {
-    const int p = part_of(j);
-    return kKT * chunks_of(p) % 256 == 0 || tid + 256 * (j - first_of(p)) < kKT * chunks_of(p);
-  };
-  u32x4_t st[NLD];
-  auto gload = [&](int kt) {
-    const int64_t t0 = s0 + static_cast<int64_t>(kt) * kKT;
-    const uint8_t* base[3] = {
-        reinterpret_cast<const uint8_t*>(a.k + t0 * a.ldk + static_cast<int64_t>(head) * DC),
-        reinterpret_cast<const uint8_t*>(a.kr + t0 * a.ldkr),
-        reinterpret_cast<const uint8_t*>(a.v + t0 * a.ldv + static_cast<int64_t>(head) * DV)};
-    const int lim = S - 1 - kt * kKT;   // the tile's last row inside the sequence
-    if (lim >= kKT - 1) {
-#pragma unroll
-      for (int j = 0; j < NLD; ++j)
-        st[j] = active(j) ? *reinterpret_cast<const u32x4_t*>(base[part_of(j)] + goff[j]) : u32x4_t{};
-    } else {
-      // the tile crosses the sequence end: rows past it read the last row
-      // (their scores are masked, so their weights are exactly zero)
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int p = part_of(j), cp = chunks_of(p);
-        const int c = tid + 256 * (j - first_of(p));
-        const int64_t ld = p == 0 ? a.ldk : (p == 1 ? a.ldkr : a.ldv);
-        const int64_t off = static_cast<int64_t>(min(c / cp, lim)) * ld * 2 + 16 * (c % cp);
-        st[j] = active(j) ? *reinterpret_cast<const u32x4_t*>(base[p] + off) : u32x4_t{};
+    for (int i = 0; i < (RG::NB + 3) / 4; ++i) {
+      const int blk = w + 4 * i;
+      if (blk >= RG::NB) break;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(rows);
+      uint32_t off;
+      if (lim >= kKT - 1) {   // every row of the tile is inside the sequence
+        src += static_cast<int64_t>(blk) * RG::R * ld * 2;
+        off = lane_off;
+      } else {                // rows past the sequence end read its last row
+        const int row = min(blk * RG::R + lane % RG::R, lim);
+        off = static_cast<uint32_t>(row * ld * 2 + 16 * (lane / RG::R));
       }
+      asm volatile("" : "+s"(src));
+      dma16(src, off, dst + blk * RG::kStride);
     }
   };
-  auto swrite = [&](int buf) {
-    const uint32_t tb = static_cast<uint32_t>(buf) * ((KTILE + VTILE) * 2);
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)
-      if (active(j))
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
-            static_cast<uintptr_t>(lds0 + tb + loff[j])) = st[j];
+  auto issue = [&](int kt, int buf) {
+    const int64_t t0 = s0 + static_cast<int64_t>(kt) * kKT;
+    const int lim = S - 1 - kt * kKT;   // the tile's last row inside the sequence
+    const uint32_t tb = lds0 + static_cast<uint32_t>(buf) * kTileBytes;
+    copy_part(RK{}, a.k + t0 * a.ldk + static_cast<int64_t>(head) * DC, a.ldk, gk, tb, lim);
+    if constexpr (CR > 0) copy_part(RR{}, a.kr + t0 * a.ldkr, a.ldkr, gr, tb + kOffR, lim);
+    copy_part(RV{}, a.v + t0 * a.ldv + static_cast<int64_t>(head) * DV, a.ldv, gv, tb + kOffV, lim);
   };
 
   f32x16_t o[DV / 32];
@@ -167,33 +170,43 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   float m_run = -INFINITY, l_lane = 0.f;
   const float c = a.c_log2;
 
-  // LDS byte addresses of this lane's fragments within a tile
-  const uint32_t tile_bytes = (KTILE + VTILE) * 2;
-  const uint32_t k_off = (l32 * PK + 8 * half) * 2;
-  // transposed value reads: 16-lane group g16, source lane s16 supplies key
-  // row 4 (g16 >> 1) + (s16 >> 2) (+8 for the upper four keys) and dims
-  // 16 (g16 & 1) + 4 (s16 & 3) .. + 3 of a 32-dim block
+  // LDS byte offsets of this lane's fragments within a tile: key fragment
+  // kc is row l32, chunk 2 kc + half of its part (the chunk term is an
+  // immediate offset); the transposed value reads of 16-lane group g16 take
+  // row 4 (g16 >> 1) + (s16 >> 2) (+8 for the upper four keys, +16 for the
+  // second 16-key step) and dims 16 (g16 & 1) + 4 (s16 & 3) .. + 3 of the
+  // 32-dim block mb
+  const uint32_t kc_off = RK::at(l32, half);
+  const uint32_t kr_off = kOffR + RR::at(l32, half);
   const int g16 = lane >> 4, s16 = lane & 15;
-  const uint32_t v_off = (KTILE + (4 * (g16 >> 1) + (s16 >> 2)) * PV + 16 * (g16 & 1) + 4 * (s16 & 3)) * 2;
+  const uint32_t v_off = kOffV + RV::at(4 * (g16 >> 1) + (s16 >> 2), 2 * (g16 & 1) + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
+  // offset of rows r0 + dr from row r0 (r0 < 8, dr a multiple of 8)
+  auto vrow = [](int dr) { return static_cast<uint32_t>((dr / RV::R) * RV::kStride + 16 * (dr % RV::R)); };
 
-  gload(0);
-  swrite(0);
+  issue(0, 0);
+  PA_WAIT_VM(0);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  // tiles from n_vis on start after the wavefront's last query: fully
+  // masked, the wavefront only takes part in their copies and barriers (two
+  // loops rather than a test in one, so that O stays in the same registers)
+  const int n_vis = min(n_kt, w_last / kKT + 1);
+  int kt = 0;
+  for (; kt < n_vis; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < n_kt;
-    if (more) gload(kt + 1);
-    // tiles that start after the wavefront's last query are fully masked
-    if (kt * kKT <= w_last) {
-      const uint32_t tb = lds0 + buf * tile_bytes;
+    // tile kt + 1 goes into the other buffer, which every wavefront finished
+    // reading before the barrier that ended the previous step
+    if (kt + 1 < n_kt) issue(kt + 1, buf ^ 1);
+    {
+      const uint32_t tb = lds0 + static_cast<uint32_t>(buf) * kTileBytes;
       // every key fragment of the tile is read before the first product (the
       // scheduling barrier keeps the compiler from interleaving the reads
       // with the products, which would expose the LDS latency at each pair)
       bf16x8_t kf[DQK / 16];
 #pragma unroll
-      for (int kc = 0; kc < DQK / 16; ++kc)
-        kf[kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            static_cast<uintptr_t>(tb + k_off + 32 * kc));
+      for (int kc = 0; kc < DQK / 16; ++kc) {
+        const uint32_t ad = kc < DC / 16 ? tb + kc_off + 32 * RK::R * kc : tb + kr_off + 32 * RR::R * (kc - DC / 16);
+        kf[kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(static_cast<uintptr_t>(ad));
+      }
       __builtin_amdgcn_sched_barrier(0);
       f32x16_t s = f32x16_t{};
 #pragma unroll
@@ -237,15 +250,22 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < DV / 32; ++mb) {
-          const uint32_t va = tb + v_off + (16 * kk * PV + 32 * mb) * 2;
+          const uint32_t va = tb + v_off + vrow(16 * kk) + 64 * RV::R * mb;
           const s16x4_t lo = tr16(va);
-          const s16x4_t hi = tr16(va + 8 * PV * 2);
+          const s16x4_t hi = tr16(va + vrow(8));
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[mb], 0, 0, 0);
         }
       }
     }
-    if (more) swrite(buf ^ 1);
+    // this wavefront's copies of tile kt + 1 have landed; after the barrier
+    // every wavefront's have
+    PA_WAIT_VM(0);
+    __syncthreads();
+  }
+  for (; kt < n_kt; ++kt) {
+    if (kt + 1 < n_kt) issue(kt + 1, (kt & 1) ^ 1);
+    PA_WAIT_VM(0);
     __syncthreads();
   }
 
