@@ -208,9 +208,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
         kf[kc] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(static_cast<uintptr_t>(ad));
       }
       __builtin_amdgcn_sched_barrier(0);
+      // the score products at raised wavefront priority: the other wavefront
+      // on the SIMD (another workgroup's) runs its softmax on the vector unit
+      // meanwhile
+      __builtin_amdgcn_s_setprio(1);
       f32x16_t s = f32x16_t{};
 #pragma unroll
       for (int kc = 0; kc < DQK / 16; ++kc) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kc], qf[kc], s, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
       // register r holds key kt * 32 + 8 (r / 4) + 4 half + r % 4 of query
       // qrow; only a tile that reaches past the wavefront's first query or the
       // sequence end needs the mask (a wave-uniform test)
