@@ -212,90 +212,124 @@ __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restri
 // accumulation), so the result keeps the precision of the fp32 weights.
 // Workgroup = 32 rows x 128 outputs (4 wavefronts x 32 outputs) over one
 // split of K; A and W tiles of 32 k go through double-buffered LDS with rows
-// padded to 33 words. Each weight element is read from memory once per row
+// padded to 36 words. Each weight element is read from memory once per row
 // block; split-K (fp32 partial tiles, summed in split order) gives the
 // skinny shapes enough workgroups to stream the weights at full bandwidth.
+//
+// Within a 32-k stage the MFMA k index is permuted: MFMA kk (0..15) takes k
+// = kk from lanes 0..31 and k = 16 + kk from lanes 32..63, so a lane's 16
+// values of a stage are contiguous (four 16-byte LDS reads per operand
+// instead of sixteen 4-byte ones); A and W use the same order, so the sums
+// are those of the plain order, term for term.
 typedef float f32x16g __attribute__((ext_vector_type(16)));
-constexpr int kSM = 32, kSN = 128, kSK = 32, kSP = kSK + 1;
+typedef float f32x4g __attribute__((ext_vector_type(4)));
+constexpr int kSM = 32, kSN = 128, kSK = 32, kSP = kSK + 4;
 
-template <int A_BF16>
+// A_BF16: activations in bf16. A_VEC: activation rows are 4-element aligned
+// (16 bytes for fp32, 8 for bf16) with a row stride that is a multiple of 4,
+// so a thread's 4 consecutive k load as one vector.
+template <int A_BF16, int A_VEC>
 __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs g, int splits, int k_per_split,
                                                           float* __restrict__ partial) {
-  __shared__ float As[2][kSM * kSP];
-  __shared__ float Ws[2][kSN * kSP];
+  __shared__ __attribute__((aligned(16))) float As[2][kSM * kSP];
+  __shared__ __attribute__((aligned(16))) float Ws[2][kSN * kSP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kSN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kSM;
   const int bz = blockIdx.z / splits, z = blockIdx.z % splits;
   const int kb = z * k_per_split, ke = min(g.K, kb + k_per_split);
-  const float* Af = static_cast<const float*>(g.A) + bz * g.sAb;
-  const uint16_t* Ah = static_cast<const uint16_t*>(g.A) + bz * g.sAb;
-  const float* W = g.B + bz * g.sBb;
-  // thread tid stages A element (row tid / 8, k 4 (tid % 8) .. + 3) and W rows
-  // tid / 8 + 32 j (j < 4), k 4 (tid % 8) .. + 3
+  // thread tid stages A row tid / 8 and W rows tid / 8 + 32 j (j < 4), k
+  // 4 (tid % 8) .. + 3 of a stage; rows past M or N read the last row (their
+  // outputs are never stored). W offsets are 32-bit byte offsets from the
+  // batch's weight base (the host checks they fit).
   const int r8 = tid >> 3, k4 = (tid & 7) * 4;
+  const int64_t am = min(m0 + r8, static_cast<int64_t>(g.M) - 1);
+  const float* Af = static_cast<const float*>(g.A) + bz * g.sAb + am * g.sAm;
+  const uint16_t* Ah = static_cast<const uint16_t*>(g.A) + bz * g.sAb + am * g.sAm;
+  const float* Wb = g.B + bz * g.sBb;
+  uint32_t woff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = min(n0 + r8 + 32 * j, static_cast<int64_t>(g.N) - 1);
+    woff[j] = static_cast<uint32_t>(n * g.sBn * 4);
+  }
   // two register sets: the loads of stage s + 2 are issued before stage s is
-  // multiplied, so each stage's loads have two stages of MFMAs to arrive
-  float ra[2][4], rw[2][4][4];
+  // multiplied, so each stage's loads have two stages of MFMAs to arrive.
+  // Every stage runs the same code (no branch around loads, so the loads'
+  // registers need no waits beyond their own): a stage at or past the
+  // split's last one re-reads that last stage (cached), and A values at k
+  // past ke are 0, which zeroes their products (the weights read there are
+  // finite: K is a multiple of 4, so no 4-element chunk reaches past a row's
+  // K values into its padding).
+  const int klast = kb + ((ke - kb - 1) / kSK) * kSK;   // the split's last stage
+  f32x4g ra[2], rw[2][4];
   auto gload = [&](auto SET, int k0) {
     constexpr int set = decltype(SET)::value;
-    const int64_t m = m0 + r8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + k4 + i;
-      float v = 0.f;
-      if (m < g.M && k < ke) v = A_BF16 ? bf16_to_f32(Ah[m * g.sAm + k]) : Af[m * g.sAm + k];
-      ra[set][i] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + r8 + 32 * j;
-      const int k = k0 + k4;
-      if (n < g.N && k + 3 < ke) {
-        const float4 v = *reinterpret_cast<const float4*>(W + n * g.sBn + k);
-        rw[set][j][0] = v.x; rw[set][j][1] = v.y; rw[set][j][2] = v.z; rw[set][j][3] = v.w;
+    // this thread's 4-element chunk, kept inside the rows' K values
+    const int kl = min(min(k0, klast) + k4, g.K - 4);
+    f32x4g a;
+    if constexpr (A_VEC) {
+      if constexpr (A_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(Ah + kl);
+        a = f32x4g{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                   __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u)};
       } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rw[set][j][i] = (n < g.N && k + i < ke) ? W[n * g.sBn + k + i] : 0.f;
+        a = *reinterpret_cast<const f32x4g*>(Af + kl);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = A_BF16 ? bf16_to_f32(Ah[kl + i]) : Af[kl + i];
     }
+    ra[set] = a;
+    const uint8_t* wk = reinterpret_cast<const uint8_t*>(Wb + kl);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rw[set][j] = *reinterpret_cast<const f32x4g*>(wk + woff[j]);
   };
-  auto swrite = [&](auto SET, int buf) {
+  // (the zeroing waits for the loads, so it is done here, where the stage's
+  // values are needed anyway)
+  auto swrite = [&](auto SET, int buf, int k0) {
     constexpr int set = decltype(SET)::value;
+    f32x4g a = ra[set];
+    if (k0 + kSK > ke) {   // a partial or past-the-end stage (wave-uniform)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) As[buf][r8 * kSP + k4 + i] = ra[set][i];
+      for (int i = 0; i < 4; ++i) a[i] = k0 + k4 + i < ke ? a[i] : 0.f;
+    }
+    *reinterpret_cast<f32x4g*>(&As[buf][r8 * kSP + k4]) = a;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ws[buf][(r8 + 32 * j) * kSP + k4 + i] = rw[set][j][i];
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4g*>(&Ws[buf][(r8 + 32 * j) * kSP + k4]) = rw[set][j];
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   f32x16g acc = f32x16g{};
-  if (kb < ke) {
+  if (kb < ke) {   // (uniform over the workgroup)
     gload(S0{}, kb);
-    if (kb + kSK < ke) gload(S1{}, kb + kSK);
-    swrite(S0{}, 0);
-  }
-  __syncthreads();
-  // stage at k0 sits in LDS buffer buf; its successor in register set 1 - SET
-  // (SET alternates with the stage, at compile time through the unrolled pair)
-  auto stage = [&](auto SET, int k0, int buf) {
-    constexpr int set = decltype(SET)::value;
-    if (k0 + 2 * kSK < ke) gload(std::integral_constant<int, set>{}, k0 + 2 * kSK);
-#pragma unroll
-    for (int kk = 0; kk < kSK / 2; ++kk) {
-      const float a = As[buf][l32 * kSP + 2 * kk + half];
-      const float b = Ws[buf][(32 * w + l32) * kSP + 2 * kk + half];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-    }
-    if (k0 + kSK < ke) swrite(std::integral_constant<int, 1 - set>{}, buf ^ 1);
+    gload(S1{}, kb + kSK);
+    swrite(S0{}, 0, kb);
     __syncthreads();
-  };
-  for (int k0 = kb; k0 < ke; k0 += 2 * kSK) {
-    stage(S0{}, k0, 0);
-    if (k0 + kSK < ke) stage(S1{}, k0 + kSK, 1);
+    // stage at k0 sits in LDS buffer buf; its successor in register set
+    // 1 - SET (SET alternates with the stage, at compile time through the
+    // unrolled pair)
+    auto stage = [&](auto SET, int k0, int buf) {
+      constexpr int set = decltype(SET)::value;
+      gload(std::integral_constant<int, set>{}, k0 + 2 * kSK);
+      f32x4g av[4], wv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = *reinterpret_cast<const f32x4g*>(&As[buf][l32 * kSP + 16 * half + 4 * q]);
+        wv[q] = *reinterpret_cast<const f32x4g*>(&Ws[buf][(32 * w + l32) * kSP + 16 * half + 4 * q]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kSK / 2; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[kk >> 2][kk & 3], wv[kk >> 2][kk & 3], acc, 0, 0, 0);
+      swrite(std::integral_constant<int, 1 - set>{}, buf ^ 1, k0 + kSK);
+      __syncthreads();
+    };
+    // stages in pairs: an odd count runs one all-zero stage more
+    for (int k0 = kb; k0 < ke; k0 += 2 * kSK) {
+      stage(S0{}, k0, 0);
+      stage(S1{}, k0 + kSK, 1);
+    }
   }
   // register r: row m0 + 8 (r / 4) + 4 half + r % 4, output n0 + 32 w + l32
   const int64_t n = n0 + 32 * w + l32;
@@ -322,8 +356,14 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int spli
 }
 
 bool skinny_ok(const GemmArgs& g) {
-  return g.sAk == 1 && g.sBk == 1 && g.sBn % 4 == 0 && g.sBb % 4 == 0 && aligned16(g.B) &&
-         g.M <= 8 * kSM;
+  // (a weight batch's row offsets are 32-bit byte offsets)
+  return g.sAk == 1 && g.sBk == 1 && g.K % 4 == 0 && g.sBn % 4 == 0 && g.sBb % 4 == 0 &&
+         aligned16(g.B) && g.M <= 8 * kSM && static_cast<int64_t>(g.N) * g.sBn * 4 < (int64_t{1} << 32);
+}
+// activation rows load 4 elements at a time
+bool skinny_a_vec(const GemmArgs& g) {
+  const uintptr_t al = g.a_bf16 ? 7u : 15u;
+  return g.sAm % 4 == 0 && g.sAb % 4 == 0 && (reinterpret_cast<uintptr_t>(g.A) & al) == 0;
 }
 
 }  // namespace
@@ -368,10 +408,15 @@ mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial, size_t
     const int gz = splits > 1 ? (g.K + kps_r - 1) / kps_r : 1;
     const dim3 grid((g.N + kSN - 1) / kSN, (g.M + kSM - 1) / kSM, static_cast<unsigned>(g.batch * gz));
     if (grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
-    if (g.a_bf16)
-      hipLaunchKernelGGL(skinny_gemm_kernel<1>, grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    const bool av = skinny_a_vec(g);
+    if (g.a_bf16 && av)
+      hipLaunchKernelGGL((skinny_gemm_kernel<1, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    else if (g.a_bf16)
+      hipLaunchKernelGGL((skinny_gemm_kernel<1, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    else if (av)
+      hipLaunchKernelGGL((skinny_gemm_kernel<0, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
     else
-      hipLaunchKernelGGL(skinny_gemm_kernel<0>, grid, dim3(256), 0, st, g, gz, kps_r, partial);
+      hipLaunchKernelGGL((skinny_gemm_kernel<0, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
     if (gz > 1) {
       const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
       const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
