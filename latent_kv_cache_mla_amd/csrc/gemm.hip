@@ -355,6 +355,23 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, int spli
   }
 }
 
+// The split sums for outputs whose rows are contiguous, 16-byte aligned and
+// a multiple of 4 long: workgroup (x, row) sums 4 consecutive outputs per
+// thread over the splits, in split order (the same order as above).
+__global__ __launch_bounds__(256) void skinny_reduce4_kernel(GemmArgs g, int splits,
+                                                             const float* __restrict__ partial) {
+  typedef float f32x4r __attribute__((ext_vector_type(4)));
+  const int row = blockIdx.y;   // b * M + m
+  const int64_t n = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (n >= g.N) return;
+  const int64_t total = static_cast<int64_t>(g.M) * g.N * g.batch;
+  const float* p = partial + static_cast<int64_t>(row) * g.N + n;
+  f32x4r s = *reinterpret_cast<const f32x4r*>(p);
+  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4r*>(p + z * total);
+  const int b = row / g.M, m = row % g.M;
+  *reinterpret_cast<f32x4r*>(g.Y + b * g.sYb + m * g.sYm + n) = s;
+}
+
 bool skinny_ok(const GemmArgs& g) {
   // (a weight batch's row offsets are 32-bit byte offsets)
   return g.sAk == 1 && g.sBk == 1 && g.K % 4 == 0 && g.sBn % 4 == 0 && g.sBb % 4 == 0 &&
@@ -418,10 +435,18 @@ mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial, size_t
     else
       hipLaunchKernelGGL((skinny_gemm_kernel<0, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
     if (gz > 1) {
-      const int64_t total = static_cast<int64_t>(g.batch) * g.M * g.N;
-      const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-      hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks), dim3(256), 0, st, g, gz,
-                         static_cast<const float*>(partial));
+      const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
+      if (g.sYn == 1 && g.N % 4 == 0 && g.sYm % 4 == 0 && g.sYb % 4 == 0 && aligned16(g.Y) &&
+          rows <= 65535) {
+        const dim3 grid4(static_cast<unsigned>((g.N / 4 + 255) / 256), static_cast<unsigned>(rows));
+        hipLaunchKernelGGL(skinny_reduce4_kernel, grid4, dim3(256), 0, st, g, gz,
+                           static_cast<const float*>(partial));
+      } else {
+        const int64_t total = rows * g.N;
+        const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+        hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks), dim3(256), 0, st, g, gz,
+                           static_cast<const float*>(partial));
+      }
     }
   } else {
     const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, g.batch);
