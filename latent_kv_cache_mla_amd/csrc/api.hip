@@ -411,7 +411,9 @@ mla_status mla_output_proj(const void* o_latent, int32_t o_dtype, int32_t T, int
 size_t mla_cache_append_workspace_size(int32_t T, int32_t d, int32_t d_c, int32_t d_rope) {
   if (T < 0 || d < 1 || d_c < 1 || d_rope < 0) return 0;
   return a256b(sizeof(float) * static_cast<size_t>(T) * (d_c + d_rope)) +
-         a256b(max2(gemm_partial_bytes(1, T, d_c, d), gemm_partial_bytes(1, T, d_rope, d))) + 256;
+         a256b(max2(gemm_partial_bytes(1, T, d_c + d_rope, d),
+                    max2(gemm_partial_bytes(1, T, d_c, d), gemm_partial_bytes(1, T, d_rope, d)))) +
+         256;
 }
 
 mla_status mla_cache_write(const float* rows, int32_t T, int32_t d_c, int32_t d_rope, float theta,
@@ -453,6 +455,16 @@ mla_status mla_cache_append(const float* h, int32_t T, int32_t d, const float* W
   g.A = h; g.a_bf16 = 0; g.sAm = d; g.sAk = 1;
   g.B = W_DKV; g.sBk = 1; g.sBn = d;
   g.Y = cr; g.sYm = L; g.sYn = 1;
+  if (d_rope > 0) {   // one GEMM over both weight matrices where the skinny path takes it
+    GemmArgs gc = g;
+    gc.N = L; gc.B2 = W_KR; gc.N1 = d_c;
+    if (skinny_ok(gc)) {
+      mla_status s = launch_gemm(gc, st, part, part_bytes);
+      if (s != MLA_OK) return s;
+      return mla_cache_write(cr, T, d_c, d_rope, theta, positions, slots, cache_dtype, cache,
+                             cache_scale, stream);
+    }
+  }
   mla_status s = launch_gemm(g, st, part, part_bytes);
   if (s != MLA_OK) return s;
   if (d_rope > 0) {
@@ -468,8 +480,11 @@ mla_status mla_cache_append(const float* h, int32_t T, int32_t d, const float* W
 size_t mla_absorb_query_workspace_size(int32_t T, int32_t d_in, int32_t n_h, int32_t d_c,
                                        int32_t d_rope) {
   if (T < 0 || d_in < 1 || n_h < 1 || d_c < 1 || d_rope < 0) return 0;
+  // the fp32 rows [q_abs | q_rope] (one GEMM over both weight matrices) and
+  // its split partials, or the two GEMMs' partials
   return a256b(sizeof(float) * static_cast<size_t>(T) * n_h * (d_c + d_rope)) +
-         a256b(max2(gemm_partial_bytes(n_h, T, d_c, d_in), gemm_partial_bytes(1, T, n_h * d_rope, d_in))) +
+         a256b(max2(gemm_partial_bytes(1, T, n_h * (d_c + d_rope), d_in),
+                    max2(gemm_partial_bytes(n_h, T, d_c, d_in), gemm_partial_bytes(1, T, n_h * d_rope, d_in)))) +
          256;
 }
 
@@ -489,16 +504,35 @@ mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MLA_ERR_MISALIGNED, "workspace must be 256-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* qa32 = static_cast<float*>(workspace);
-  float* qr32 = qa32 + static_cast<size_t>(T) * n_h * d_c;
+  float* q32 = static_cast<float*>(workspace);
   const size_t q_bytes = a256b(sizeof(float) * static_cast<size_t>(T) * n_h * (d_c + d_rope));
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + q_bytes);
   const size_t part_bytes = workspace_bytes - q_bytes;
+  // One GEMM over both weight matrices (W_qabs for the first n_h d_c columns,
+  // W_QR for the rest) into rows [q_abs | q_rope]; the finish pass sums its
+  // split partials, applies RoPE and converts.
+  const int64_t ld = static_cast<int64_t>(n_h) * (d_c + d_rope);
+  GemmArgs gc{};
+  gc.batch = 1; gc.M = T; gc.N = static_cast<int>(ld); gc.K = d_in;
+  gc.A = x; gc.a_bf16 = 0; gc.sAm = d_in; gc.sAk = 1;
+  gc.B = W_qabs; gc.sBk = 1; gc.sBn = d_in;
+  gc.Y = q32; gc.sYm = ld; gc.sYn = 1;
+  if (d_rope > 0) { gc.B2 = W_QR; gc.N1 = n_h * d_c; }
+  if (ld <= INT32_MAX && skinny_ok(gc)) {
+    int splits = 1;
+    mla_status s = launch_skinny(gc, st, part, part_bytes, &splits);
+    if (s != MLA_OK) return s;
+    return splits > 1 ? launch_query_finish(part, ld, splits, static_cast<int64_t>(T) * ld, T, n_h, d_c,
+                                            d_rope, theta, positions, q_dtype, q_abs, q_rope, st)
+                      : launch_query_finish(q32, ld, 1, 0, T, n_h, d_c, d_rope, theta, positions, q_dtype,
+                                            q_abs, q_rope, st);
+  }
+  // other shapes: one GEMM per weight matrix, each with its own split sums
   GemmArgs g{};
   g.batch = n_h; g.M = T; g.N = d_c; g.K = d_in;
   g.A = x; g.a_bf16 = 0; g.sAb = 0; g.sAm = d_in; g.sAk = 1;
   g.B = W_qabs; g.sBb = static_cast<int64_t>(d_c) * d_in; g.sBk = 1; g.sBn = d_in;
-  g.Y = qa32; g.sYb = d_c; g.sYm = static_cast<int64_t>(n_h) * d_c; g.sYn = 1;
+  g.Y = q32; g.sYb = d_c; g.sYm = ld; g.sYn = 1;
   mla_status s = launch_gemm(g, st, part, part_bytes);
   if (s != MLA_OK) return s;
   if (d_rope > 0) {
@@ -506,11 +540,11 @@ mla_status mla_absorb_query(const float* x, int32_t T, int32_t d_in, const float
     g2.batch = 1; g2.M = T; g2.N = n_h * d_rope; g2.K = d_in;
     g2.A = x; g2.a_bf16 = 0; g2.sAm = d_in; g2.sAk = 1;
     g2.B = W_QR; g2.sBk = 1; g2.sBn = d_in;
-    g2.Y = qr32; g2.sYm = static_cast<int64_t>(n_h) * d_rope; g2.sYn = 1;
+    g2.Y = q32 + static_cast<int64_t>(n_h) * d_c; g2.sYm = ld; g2.sYn = 1;
     s = launch_gemm(g2, st, part, part_bytes);
     if (s != MLA_OK) return s;
   }
-  return launch_query_finish(qa32, qr32, T, n_h, d_c, d_rope, theta, positions, q_dtype, q_abs,
+  return launch_query_finish(q32, ld, 1, 0, T, n_h, d_c, d_rope, theta, positions, q_dtype, q_abs,
                              q_rope, st);
 }
 

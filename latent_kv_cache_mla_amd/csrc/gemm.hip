@@ -164,10 +164,13 @@ __global__ __launch_bounds__(256) void append_finish_kernel(const float* __restr
 // Block (token t, slice y of gridDim.y): convert a slice of q_abs, and rotate
 // q^R of the heads of the slice. The rotation of pair k depends only on the
 // token's position, so its cosine and sine are computed once per block (the
-// first d_r / 2 threads, fp64) and shared through LDS.
+// first d_r / 2 threads, fp64) and shared through LDS. The source row of
+// token t is q32 + t ld: n_h d_c values of q_abs, then n_h d_r of q_rope,
+// summed over `splits` copies split_stride apart (the split sums of the
+// projection, in split order).
 template <int QT>
-__global__ __launch_bounds__(256) void query_finish_kernel(const float* __restrict__ qa32,
-                                                           const float* __restrict__ qr32, int n_h,
+__global__ __launch_bounds__(256) void query_finish_kernel(const float* __restrict__ q32, int64_t ld,
+                                                           int splits, int64_t split_stride, int n_h,
                                                            int d_c, int d_r, double theta,
                                                            const int32_t* __restrict__ positions,
                                                            void* __restrict__ q_abs,
@@ -178,13 +181,39 @@ __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restri
   const int half = d_r / 2;
   for (int k = threadIdx.x; k < half; k += 256) rope_cs(pos, k, d_r, theta, &cs_lds[0][k], &cs_lds[1][k]);
   __syncthreads();
+  const float* row = q32 + t * ld;
+  auto src = [&](int64_t i) {
+    float v = row[i];
+    for (int z = 1; z < splits; ++z) v += row[z * split_stride + i];
+    return v;
+  };
   const int64_t na = static_cast<int64_t>(n_h) * d_c;
   const int64_t per = (na + gridDim.y - 1) / gridDim.y;
   const int64_t i0 = blockIdx.y * per, i1 = min(na, i0 + per);
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
-    const float v = qa32[t * na + i];
-    if constexpr (QT == MLA_FP32) static_cast<float*>(q_abs)[t * na + i] = v;
-    else static_cast<uint16_t*>(q_abs)[t * na + i] = f32_to_bf16(v);
+  // 4 values per thread where rows, slices and split copies are 16-byte
+  // aligned (all loads of a thread issued before they are summed)
+  const uintptr_t out_al = QT == MLA_FP32 ? 15u : 7u;
+  const bool vec = ((reinterpret_cast<uintptr_t>(q32) | (ld * 4) | (split_stride * 4) | (per * 4)) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(q_abs) & out_al) == 0 && na % 4 == 0 && (i1 - i0) % 4 == 0;
+  if (vec) {
+    typedef float f32x4q __attribute__((ext_vector_type(4)));
+    for (int64_t i = i0 + 4 * threadIdx.x; i < i1; i += 4 * 256) {
+      f32x4q v = *reinterpret_cast<const f32x4q*>(row + i);
+      for (int z = 1; z < splits; ++z) v += *reinterpret_cast<const f32x4q*>(row + z * split_stride + i);
+      if constexpr (QT == MLA_FP32) {
+        *reinterpret_cast<f32x4q*>(static_cast<float*>(q_abs) + t * na + i) = v;
+      } else {
+        const uint32_t lo = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+        const uint32_t hi = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(q_abs) + t * na + i) = make_uint2(lo, hi);
+      }
+    }
+  } else {
+    for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) {
+      const float v = src(i);
+      if constexpr (QT == MLA_FP32) static_cast<float*>(q_abs)[t * na + i] = v;
+      else static_cast<uint16_t*>(q_abs)[t * na + i] = f32_to_bf16(v);
+    }
   }
   const int hp = (n_h + gridDim.y - 1) / gridDim.y;
   const int h0 = blockIdx.y * hp, h1 = min(n_h, h0 + hp);
@@ -192,7 +221,8 @@ __global__ __launch_bounds__(256) void query_finish_kernel(const float* __restri
     const int h = h0 + i / half, k = i % half;
     const float c = cs_lds[0][k], s = cs_lds[1][k];
     const int64_t base = (t * n_h + h) * d_r;
-    const float x0 = qr32[base + 2 * k], x1 = qr32[base + 2 * k + 1];
+    const int64_t sb = na + static_cast<int64_t>(h) * d_r;
+    const float x0 = src(sb + 2 * k), x1 = src(sb + 2 * k + 1);
     const float y0 = x0 * c - x1 * s, y1 = x0 * s + x1 * c;
     if constexpr (QT == MLA_FP32) {
       static_cast<float*>(q_rope)[base + 2 * k] = y0;
@@ -247,11 +277,16 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(GemmArgs g, int splits
   const int64_t am = min(m0 + r8, static_cast<int64_t>(g.M) - 1);
   const float* Af = static_cast<const float*>(g.A) + bz * g.sAb + am * g.sAm;
   const uint16_t* Ah = static_cast<const uint16_t*>(g.A) + bz * g.sAb + am * g.sAm;
-  const float* Wb = g.B + bz * g.sBb;
+  // the workgroup's weight matrix: B, or B2 for the columns from N1 on (N1
+  // is a multiple of 128, so a workgroup never straddles the two)
+  const bool second = g.B2 != nullptr && n0 >= g.N1;
+  const float* Wb = second ? g.B2 : g.B + bz * g.sBb;
+  const int64_t wn0 = second ? n0 - g.N1 : n0;
+  const int64_t wrows = g.B2 == nullptr ? g.N : (second ? g.N - g.N1 : g.N1);
   uint32_t woff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t n = min(n0 + r8 + 32 * j, static_cast<int64_t>(g.N) - 1);
+    const int64_t n = min(wn0 + r8 + 32 * j, wrows - 1);
     woff[j] = static_cast<uint32_t>(n * g.sBn * 4);
   }
   // two register sets: the loads of stage s + 2 are issued before stage s is
@@ -372,11 +407,17 @@ __global__ __launch_bounds__(256) void skinny_reduce4_kernel(GemmArgs g, int spl
   *reinterpret_cast<f32x4r*>(g.Y + b * g.sYb + m * g.sYm + n) = s;
 }
 
+}  // namespace
+
 bool skinny_ok(const GemmArgs& g) {
   // (a weight batch's row offsets are 32-bit byte offsets)
-  return g.sAk == 1 && g.sBk == 1 && g.K % 4 == 0 && g.sBn % 4 == 0 && g.sBb % 4 == 0 &&
+  const bool b2 = g.B2 == nullptr ||
+                  (g.batch == 1 && g.N1 > 0 && g.N1 % kSN == 0 && g.N1 < g.N && aligned16(g.B2));
+  return b2 && g.sAk == 1 && g.sBk == 1 && g.K % 4 == 0 && g.sBn % 4 == 0 && g.sBb % 4 == 0 &&
          aligned16(g.B) && g.M <= 8 * kSM && static_cast<int64_t>(g.N) * g.sBn * 4 < (int64_t{1} << 32);
 }
+
+namespace {
 // activation rows load 4 elements at a time
 bool skinny_a_vec(const GemmArgs& g) {
   const uintptr_t al = g.a_bf16 ? 7u : 15u;
@@ -415,25 +456,39 @@ size_t gemm_partial_bytes(int batch, int M, int N, int K) {
   return s > 1 ? sizeof(float) * static_cast<size_t>(s) * batch * M * N : 0;
 }
 
+mla_status launch_skinny(const GemmArgs& g, hipStream_t st, float* partial, size_t partial_bytes,
+                         int* splits) {
+  *splits = 1;
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return MLA_OK;
+  if (!skinny_ok(g)) return fail(MLA_ERR_UNSUPPORTED, "skinny gemm: unsupported operands");
+  int sp = skinny_splits(g.batch, g.M, g.N, g.K);
+  if (partial == nullptr || gemm_partial_bytes(g.batch, g.M, g.N, g.K) > partial_bytes) sp = 1;
+  const int kps = (g.K + sp - 1) / sp;
+  const int kps_r = (kps + kSK - 1) / kSK * kSK;
+  const int gz = sp > 1 ? (g.K + kps_r - 1) / kps_r : 1;
+  const dim3 grid((g.N + kSN - 1) / kSN, (g.M + kSM - 1) / kSM, static_cast<unsigned>(g.batch * gz));
+  if (grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
+  const bool av = skinny_a_vec(g);
+  if (g.a_bf16 && av)
+    hipLaunchKernelGGL((skinny_gemm_kernel<1, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+  else if (g.a_bf16)
+    hipLaunchKernelGGL((skinny_gemm_kernel<1, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+  else if (av)
+    hipLaunchKernelGGL((skinny_gemm_kernel<0, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+  else
+    hipLaunchKernelGGL((skinny_gemm_kernel<0, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+  *splits = gz;
+  return MLA_OK;
+}
+
 mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial, size_t partial_bytes) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return MLA_OK;
   if (skinny_ok(g)) {
-    int splits = skinny_splits(g.batch, g.M, g.N, g.K);
-    if (partial == nullptr || gemm_partial_bytes(g.batch, g.M, g.N, g.K) > partial_bytes) splits = 1;
-    const int kps = (g.K + splits - 1) / splits;
-    const int kps_r = (kps + kSK - 1) / kSK * kSK;
-    const int gz = splits > 1 ? (g.K + kps_r - 1) / kps_r : 1;
-    const dim3 grid((g.N + kSN - 1) / kSN, (g.M + kSM - 1) / kSM, static_cast<unsigned>(g.batch * gz));
-    if (grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
-    const bool av = skinny_a_vec(g);
-    if (g.a_bf16 && av)
-      hipLaunchKernelGGL((skinny_gemm_kernel<1, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
-    else if (g.a_bf16)
-      hipLaunchKernelGGL((skinny_gemm_kernel<1, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
-    else if (av)
-      hipLaunchKernelGGL((skinny_gemm_kernel<0, 1>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
-    else
-      hipLaunchKernelGGL((skinny_gemm_kernel<0, 0>), grid, dim3(256), 0, st, g, gz, kps_r, partial);
+    int gz = 1;
+    const mla_status s = launch_skinny(g, st, partial, partial_bytes, &gz);
+    if (s != MLA_OK) return s;
     if (gz > 1) {
       const int64_t rows = static_cast<int64_t>(g.batch) * g.M;
       if (g.sYn == 1 && g.N % 4 == 0 && g.sYm % 4 == 0 && g.sYb % 4 == 0 && aligned16(g.Y) &&
@@ -449,6 +504,7 @@ mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial, size_t
       }
     }
   } else {
+    if (g.B2 != nullptr) return fail(MLA_ERR_UNSUPPORTED, "gemm: two weight matrices need the skinny path");
     const dim3 grid((g.N + kT - 1) / kT, (g.M + kT - 1) / kT, g.batch);
     if (grid.y > 65535u || grid.z > 65535u) return fail(MLA_ERR_UNSUPPORTED, "gemm too large");
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, g);
@@ -478,8 +534,8 @@ mla_status launch_append_finish(const float* cr, int T, int d_c, int d_rope, flo
   return MLA_OK;
 }
 
-mla_status launch_query_finish(const float* q_abs32, const float* q_rope32, int T, int n_h,
-                               int d_c, int d_rope, float theta, const int32_t* positions,
+mla_status launch_query_finish(const float* q32, int64_t ld, int splits, int64_t split_stride, int T,
+                               int n_h, int d_c, int d_rope, float theta, const int32_t* positions,
                                int q_dtype, void* q_abs, void* q_rope, hipStream_t st) {
   if (T <= 0) return MLA_OK;
   if (d_rope > 256) return fail(MLA_ERR_UNSUPPORTED, "query finish: d_rope above 256");
@@ -488,11 +544,11 @@ mla_status launch_query_finish(const float* q_abs32, const float* q_rope32, int 
   const int ny = n_h < 16 ? n_h : 16;
   const dim3 grid(static_cast<unsigned>(T), static_cast<unsigned>(ny));
   if (q_dtype == MLA_FP32)
-    hipLaunchKernelGGL(query_finish_kernel<MLA_FP32>, grid, dim3(256), 0, st, q_abs32, q_rope32,
-                       n_h, d_c, d_rope, th, positions, q_abs, q_rope);
+    hipLaunchKernelGGL(query_finish_kernel<MLA_FP32>, grid, dim3(256), 0, st, q32, ld, splits,
+                       split_stride, n_h, d_c, d_rope, th, positions, q_abs, q_rope);
   else
-    hipLaunchKernelGGL(query_finish_kernel<MLA_BF16>, grid, dim3(256), 0, st, q_abs32, q_rope32,
-                       n_h, d_c, d_rope, th, positions, q_abs, q_rope);
+    hipLaunchKernelGGL(query_finish_kernel<MLA_BF16>, grid, dim3(256), 0, st, q32, ld, splits,
+                       split_stride, n_h, d_c, d_rope, th, positions, q_abs, q_rope);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "query finish launch: %s", hipGetErrorString(e));
   return MLA_OK;

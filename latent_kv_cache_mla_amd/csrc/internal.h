@@ -77,11 +77,15 @@ mla_status launch_combine(const DecodeArgs& a, hipStream_t st);
 
 // fp32 strided batched GEMM: Y[b][m][n] = sum_k A[b](m,k) * B[b](k,n)
 // with element (m,k) of A at A + b*sAb + m*sAm + k*sAk (same for B, Y).
+// With B2 set (batch 1 only), output columns n >= N1 take their weight row
+// n - N1 from B2 (same row stride) instead of B: two weight matrices that
+// share the activations in one launch.
 struct GemmArgs {
   int batch, M, N, K;
   const void* A; int a_bf16; int64_t sAb, sAm, sAk;
   const float* B; int64_t sBb, sBk, sBn;
   float* Y; int64_t sYb, sYm, sYn;
+  const float* B2 = nullptr; int N1 = 0;
 };
 // Row counts up to 256 with operands contiguous along k run on the fp32
 // matrix cores with split-K when `partial` holds gemm_partial_bytes (else
@@ -90,6 +94,13 @@ mla_status launch_gemm(const GemmArgs& g, hipStream_t st, float* partial = nullp
                        size_t partial_bytes = 0);
 size_t gemm_partial_bytes(int batch, int M, int N, int K);
 int skinny_splits(int batch, int M, int N, int K);
+// The skinny matrix-core GEMM alone (skinny_ok shapes), without the split
+// sums: with *splits > 1 on return the result is the sum over z < *splits of
+// partial[z * batch * M * N + (b * M + m) * N + n]; with *splits == 1 it is
+// in Y.
+bool skinny_ok(const GemmArgs& g);
+mla_status launch_skinny(const GemmArgs& g, hipStream_t st, float* partial, size_t partial_bytes,
+                         int* splits);
 
 // bf16 matrix-core GEMM: C[m, n] = sum_k A[m, k] B[n, k] with A [M, K] (row
 // stride lda) and B [N, K] (row stride ldb) in bf16, fp32 accumulation, C in
@@ -131,8 +142,10 @@ mla_status launch_append_finish(const float* cr, int T, int d_c, int d_rope, flo
                                 const int32_t* positions, const int32_t* slots,
                                 int cache_dtype, void* cache, float* cache_scale,
                                 hipStream_t st);
-mla_status launch_query_finish(const float* q_abs32, const float* q_rope32, int T, int n_h,
-                               int d_c, int d_rope, float theta, const int32_t* positions,
+// q32 rows of n_h (d_c + d_rope) values (q_abs, then q_rope), row stride
+// ld, summed over `splits` copies split_stride apart.
+mla_status launch_query_finish(const float* q32, int64_t ld, int splits, int64_t split_stride, int T,
+                               int n_h, int d_c, int d_rope, float theta, const int32_t* positions,
                                int q_dtype, void* q_abs, void* q_rope, hipStream_t st);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
