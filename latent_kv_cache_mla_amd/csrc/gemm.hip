@@ -402,7 +402,16 @@ __global__ __launch_bounds__(256) void skinny_reduce4_kernel(GemmArgs g, int spl
   const int64_t total = static_cast<int64_t>(g.M) * g.N * g.batch;
   const float* p = partial + static_cast<int64_t>(row) * g.N + n;
   f32x4r s = *reinterpret_cast<const f32x4r*>(p);
-  for (int z = 1; z < splits; ++z) s += *reinterpret_cast<const f32x4r*>(p + z * total);
+  // eight splits' loads in flight at a time, added in split order
+  for (int z0 = 1; z0 < splits; z0 += 8) {
+    f32x4r v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) v[u] = *reinterpret_cast<const f32x4r*>(p + (z0 + u) * total);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z0 + u < splits) s += v[u];
+  }
   const int b = row / g.M, m = row % g.M;
   *reinterpret_cast<f32x4r*>(g.Y + b * g.sYb + m * g.sYm + n) = s;
 }
