@@ -45,26 +45,39 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
   const int ke = min(g.K, kb + k_per_split);
 
   // thread tid loads 16-byte chunks c = tid + 256 j (j < 4) of each tile:
-  // row c / 8, elements 8 (c % 8) .. + 7
-  uint4 ra[4], rb[4];
+  // row c / 8 = tid / 8 + 32 j, elements 8 (tid % 8) .. + 7. The row
+  // pointers are formed once; rows past M or N read the last row (their
+  // outputs are not stored). Every stage runs the same loads: a chunk at or
+  // past K reads the row's last chunk instead (finite values), and A chunks
+  // at or past the split's end are zeroed when the stage is stored to LDS,
+  // which zeroes their products.
+  const int r8 = tid >> 3, kc = (tid & 7) * 8;
+  const uint16_t* pa[4];
+  const uint16_t* pb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pa[j] = g.A + min(m0 + r8 + 32 * j, static_cast<int64_t>(g.M) - 1) * g.lda + kc;
+    pb[j] = g.B + min(n0 + r8 + 32 * j, static_cast<int64_t>(g.N) - 1) * g.ldb + kc;
+  }
+  const int klim = g.K - 8 - kc;   // the last chunk start of a row, minus kc
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t ra[4], rb[4];
   auto gload = [&](int k0) {
+    const int kk = min(k0, klim);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
-      const int k = k0 + kc;
-      const int64_t m = m0 + row, n = n0 + row;
-      ra[j] = (m < g.M && k < ke) ? *reinterpret_cast<const uint4*>(g.A + m * g.lda + k)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-      rb[j] = (n < g.N && k < ke) ? *reinterpret_cast<const uint4*>(g.B + n * g.ldb + k)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+      ra[j] = *reinterpret_cast<const u32x4_t*>(pa[j] + kk);
+      rb[j] = *reinterpret_cast<const u32x4_t*>(pb[j] + kk);
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, int k0) {
+    // 0 for A chunks at or past the split's end (the first test is uniform)
+    const uint32_t keep = k0 + kBK > ke && k0 + kc >= ke ? 0u : ~0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = tid + 256 * j, row = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[buf][row * kPitch + kc]) = ra[j];
-      *reinterpret_cast<uint4*>(&Bs[buf][row * kPitch + kc]) = rb[j];
+      const int row = r8 + 32 * j;
+      *reinterpret_cast<u32x4_t*>(&As[buf][row * kPitch + kc]) = ra[j] & keep;
+      *reinterpret_cast<u32x4_t*>(&Bs[buf][row * kPitch + kc]) = rb[j];
     }
   };
 
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
 
   if (kb < ke) {
     gload(kb);
-    swrite(0);
+    swrite(0, kb);
   }
   __syncthreads();
   int buf = 0;
@@ -98,31 +111,38 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) swrite(buf ^ 1);
+    if (more) swrite(buf ^ 1, k0 + kBK);
     __syncthreads();
     buf ^= 1;
   }
 
   // acc[i][j] register r holds C[m][n] with m = 8 (r / 4) + 4 half + r % 4 and
-  // n = l32 within the 32 x 32 tile (i, j)
+  // n = l32 within the 32 x 32 tile (i, j). One pass per output form; the
+  // row offsets are uniform multiples of the row stride, and only a tile at
+  // the edge of C tests bounds.
+  const bool edge = m0 + kBM > g.M || n0 + kBN > g.N;
+  const int64_t mw = m0 + wm * 64 + 4 * half, nw = n0 + wn * 64 + l32;
+  auto store_all = [&](auto* base, int64_t ld, auto put) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) {
+        auto* t = base + (mw + i * 32) * ld + nw + j * 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int64_t n = n0 + wn * 64 + j * 32 + l32;
-        if (m >= g.M || n >= g.N) continue;
-        const float v = acc[i][j][r];
-        if (g.splits > 1) {
-          g.partial[(static_cast<int64_t>(kz) * g.M + m) * g.N + n] = v;
-        } else if (g.c_bf16) {
-          static_cast<uint16_t*>(g.C)[m * g.ldc + n] = f32_to_bf16(v);
-        } else {
-          static_cast<float*>(g.C)[m * g.ldc + n] = v;
+        for (int r = 0; r < 16; ++r) {
+          const int dm = 8 * (r >> 2) + (r & 3);
+          if (edge && (mw + i * 32 + dm >= g.M || nw + j * 32 >= g.N)) continue;
+          put(t + dm * ld, acc[i][j][r]);
         }
       }
+  };
+  if (g.splits > 1)
+    store_all(g.partial + static_cast<int64_t>(kz) * g.M * g.N, static_cast<int64_t>(g.N),
+              [](float* q, float v) { *q = v; });
+  else if (g.c_bf16)
+    store_all(static_cast<uint16_t*>(g.C), g.ldc, [](uint16_t* q, float v) { *q = f32_to_bf16(v); });
+  else
+    store_all(static_cast<float*>(g.C), g.ldc, [](float* q, float v) { *q = v; });
 }
 
 // ---- large-tile variant: 256 x 256 output tile, one wavefront per SIMD ----
