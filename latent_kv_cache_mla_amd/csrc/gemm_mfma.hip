@@ -347,6 +347,36 @@ __global__ __launch_bounds__(256) void gemm_split_reduce(MfmaGemmArgs g) {
   }
 }
 
+// The split sums for C rows of a multiple of 4 outputs with 16-byte (fp32)
+// or 8-byte (bf16) aligned rows: workgroup (x, row) sums 4 consecutive
+// outputs per thread, every split's loads issued before the sums, added in
+// split order (the same order as above).
+__global__ __launch_bounds__(256) void gemm_split_reduce4(MfmaGemmArgs g) {
+  typedef float f32x4s __attribute__((ext_vector_type(4)));
+  const int64_t m = blockIdx.y;
+  const int64_t n = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (n >= g.N) return;
+  const int64_t total = static_cast<int64_t>(g.M) * g.N;
+  const float* p = g.partial + m * g.N + n;
+  f32x4s s = *reinterpret_cast<const f32x4s*>(p);
+  for (int z0 = 1; z0 < g.splits; z0 += 4) {
+    f32x4s v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (z0 + u < g.splits) v[u] = *reinterpret_cast<const f32x4s*>(p + (z0 + u) * total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (z0 + u < g.splits) s += v[u];
+  }
+  if (g.c_bf16) {
+    const uint32_t lo = f32_to_bf16(s[0]) | (static_cast<uint32_t>(f32_to_bf16(s[1])) << 16);
+    const uint32_t hi = f32_to_bf16(s[2]) | (static_cast<uint32_t>(f32_to_bf16(s[3])) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + m * g.ldc + n) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<f32x4s*>(static_cast<float*>(g.C) + m * g.ldc + n) = s;
+  }
+}
+
 }  // namespace
 
 int gemm_bf16_k_per_split(int K, int splits) {
@@ -387,9 +417,16 @@ mla_status launch_gemm_bf16(const MfmaGemmArgs& g, hipStream_t st) {
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(256), 0, st, a, kps);
   }
   if (gz > 1) {
-    const int64_t total = static_cast<int64_t>(g.M) * g.N;
-    const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    hipLaunchKernelGGL(gemm_split_reduce, dim3(blocks), dim3(256), 0, st, a);
+    const uintptr_t al = g.c_bf16 ? 7u : 15u;
+    if (g.N % 4 == 0 && g.ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(g.C) & al) == 0 &&
+        aligned16(g.partial) && g.M <= 65535) {
+      const dim3 grid4(static_cast<unsigned>((g.N / 4 + 255) / 256), static_cast<unsigned>(g.M));
+      hipLaunchKernelGGL(gemm_split_reduce4, grid4, dim3(256), 0, st, a);
+    } else {
+      const int64_t total = static_cast<int64_t>(g.M) * g.N;
+      const unsigned blocks = static_cast<unsigned>((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+      hipLaunchKernelGGL(gemm_split_reduce, dim3(blocks), dim3(256), 0, st, a);
+    }
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "bf16 GEMM launch: %s", hipGetErrorString(e));
