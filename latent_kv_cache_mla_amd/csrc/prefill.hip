@@ -328,12 +328,19 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
     x = xb;
     din = d->d_cq;
   }
-  // 3. [q^C ; q^R] for every head, q^R rotated per head, rounded to bf16
+  // 3. [q^C ; q^R] for every head into the bf16 rows qb: q^C = W^UQ x
+  // straight to bf16 (the GEMM rounds), q^R = W^QR x in fp32 (compact rows
+  // of n_h d_R), then rotated per head and rounded into its columns of qb.
   const int QW = nh * (dh + dr);
-  if ((s = gemm(T32, QW, din, x, din, w->W_UQR, din, q32, QW, 0)) != MLA_OK) return s;
-  if ((s = launch_rope_round(q32, QW, QW, nh * dh, dr > 0 ? nh : 0, dr > 0 ? dr : 2, positions,
-                             d->rope_theta, qb, QW, 0, T, st)) != MLA_OK)
-    return s;
+  const int QC = nh * dh, QR = nh * dr;
+  if ((s = gemm(T32, QC, din, x, din, w->W_UQR, din, qb, QW, 1)) != MLA_OK) return s;
+  if (dr > 0) {
+    const uint16_t* wqr = static_cast<const uint16_t*>(w->W_UQR) + static_cast<int64_t>(QC) * din;
+    if ((s = gemm(T32, QR, din, x, din, wqr, din, q32, QR, 0)) != MLA_OK) return s;
+    if ((s = launch_rope_round(q32, QR, QR, 0, nh, dr, positions, d->rope_theta, qb + QC, QW, 0, T,
+                               st)) != MLA_OK)
+      return s;
+  }
   // 4. expanded keys and values [k^C ; v] = [W^UK ; W^UV] c
   if ((s = gemm(T32, 2 * nh * dh, dc, cb, dc, w->W_UKV, dc, kv, 2 * nh * dh, 1)) != MLA_OK) return s;
   // 5. causal attention per head
