@@ -263,11 +263,19 @@ def mla_decode_validate(desc, seq_lens, block_table, n_pages, stream=None):
 
 
 def mla_fold_query(W_UQ, W_UK, n_h, d_h, d_c, d_in, W_qabs, stream=None):
+    w = "mla_fold_query"
+    _need(W_UQ, 4 * n_h * d_h * d_in, "W_UQ", w)
+    _need(W_UK, 4 * n_h * d_h * d_c, "W_UK", w)
+    _need(W_qabs, 4 * n_h * d_c * d_in, "W_qabs", w)
     _check(lib.mla_fold_query(_ptr(W_UQ), _ptr(W_UK), n_h, d_h, d_c, d_in, _ptr(W_qabs),
                               _stream(stream)), "mla_fold_query")
 
 
 def mla_fold_output(W_O, W_UV, n_h, d_h, d_c, d, W_ov, stream=None):
+    w = "mla_fold_output"
+    _need(W_O, 4 * d * n_h * d_h, "W_O", w)
+    _need(W_UV, 4 * n_h * d_h * d_c, "W_UV", w)
+    _need(W_ov, 4 * d * n_h * d_c, "W_ov", w)
     _check(lib.mla_fold_output(_ptr(W_O), _ptr(W_UV), n_h, d_h, d_c, d, _ptr(W_ov),
                                _stream(stream)), "mla_fold_output")
 
@@ -278,6 +286,14 @@ def mla_output_proj_workspace_size(T, n_h, d_c, d_h, d, mode):
 
 def mla_output_proj(o_latent, o_dtype, T, n_h, d_c, d_h, d, mode, W1, W2, out, workspace=None,
                     stream=None):
+    w = "mla_output_proj"
+    _need(o_latent, _ELEM.get(int(o_dtype), 4) * T * n_h * d_c, "o_latent", w)
+    if int(mode) == MLA_PROJ_TWO_STAGE:
+        _need(W1, 4 * n_h * d_h * d_c, "W1 (W_UV)", w)
+        _need(W2, 4 * d * n_h * d_h, "W2 (W_O)", w)
+    else:
+        _need(W1, 4 * d * n_h * d_c, "W1 (W_ov)", w)
+    _need(out, 4 * T * d, "out", w)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.mla_output_proj(_ptr(o_latent), o_dtype, T, n_h, d_c, d_h, d, mode, _ptr(W1),
                                _ptr(W2), _ptr(out), _ptr(workspace), nbytes, _stream(stream)),
@@ -286,6 +302,10 @@ def mla_output_proj(o_latent, o_dtype, T, n_h, d_c, d_h, d, mode, W1, W2, out, w
 
 def mla_cache_write(rows, T, d_c, d_rope, theta, positions, slots, cache_dtype, cache,
                     cache_scale=None, stream=None):
+    w = "mla_cache_write"
+    _need(rows, 4 * T * (d_c + d_rope), "rows", w)
+    _need(positions, 4 * T, "positions", w)
+    _need(slots, 4 * T, "slots", w)
     _check(lib.mla_cache_write(_ptr(rows), T, d_c, d_rope, float(theta), _ptr(positions),
                                _ptr(slots), cache_dtype, _ptr(cache), _ptr(cache_scale),
                                _stream(stream)), "mla_cache_write")
@@ -297,6 +317,12 @@ def mla_cache_append_workspace_size(T, d, d_c, d_rope):
 
 def mla_cache_append(h, T, d, W_DKV, W_KR, d_c, d_rope, theta, positions, slots, cache_dtype,
                      cache, cache_scale, workspace, stream=None):
+    w = "mla_cache_append"
+    _need(h, 4 * T * d, "h", w)
+    _need(W_DKV, 4 * d_c * d, "W_DKV", w)
+    _need(W_KR, 4 * d_rope * d, "W_KR", w)
+    _need(positions, 4 * T, "positions", w)
+    _need(slots, 4 * T, "slots", w)
     _check(lib.mla_cache_append(_ptr(h), T, d, _ptr(W_DKV), _ptr(W_KR), d_c, d_rope,
                                 float(theta), _ptr(positions), _ptr(slots), cache_dtype,
                                 _ptr(cache), _ptr(cache_scale), _ptr(workspace),
@@ -310,6 +336,14 @@ def mla_absorb_query_workspace_size(T, d_in, n_h, d_c, d_rope):
 
 def mla_absorb_query(x, T, d_in, W_qabs, W_QR, n_h, d_c, d_rope, theta, positions, q_dtype,
                      q_abs, q_rope, workspace, stream=None):
+    w = "mla_absorb_query"
+    qe = _ELEM.get(int(q_dtype), 4)
+    _need(x, 4 * T * d_in, "x", w)
+    _need(W_qabs, 4 * n_h * d_c * d_in, "W_qabs", w)
+    _need(W_QR, 4 * n_h * d_rope * d_in, "W_QR", w)
+    _need(positions, 4 * T, "positions", w)
+    _need(q_abs, qe * T * n_h * d_c, "q_abs", w)
+    _need(q_rope, qe * T * n_h * d_rope, "q_rope", w)
     _check(lib.mla_absorb_query(_ptr(x), T, d_in, _ptr(W_qabs), _ptr(W_QR), n_h, d_c, d_rope,
                                 float(theta), _ptr(positions), q_dtype, _ptr(q_abs),
                                 _ptr(q_rope), _ptr(workspace),

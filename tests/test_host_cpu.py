@@ -247,3 +247,38 @@ def test_noalloc_decode_rejects_calls_above_its_array(m):
                         (128, 2, 8192, "fp8")):
         d = m.decode_desc(B, q, 128, 512, 64, (S + 63) // 64, dt, "bf16", "bf16")
         assert m.mla_decode_workspace_size(d) <= m.mla_decode_noalloc_max_workspace()
+
+
+def test_binding_rejects_short_buffers_before_the_call(m):
+    """The marshalling layer compares every buffer the shapes determine with
+    what the call reads or writes through it, and raises before the C call:
+    a short buffer would otherwise be an out-of-bounds device access. CPU
+    tensors suffice: nothing reaches the library."""
+    import torch
+
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)  # noqa: E731
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
+    T, n_h, d_c, d_r, d_in, d_h, d = 4, 2, 8, 4, 16, 8, 32
+    cases = [
+        lambda: m.mla_absorb_query(f32(T * d_in), T, d_in, f32(n_h * d_c * d_in), f32(n_h * d_r * d_in),
+                                   n_h, d_c, d_r, 1e4, i32(T), m.MLA_FP32, f32(T * n_h * d_c - 1),
+                                   f32(T * n_h * d_r), f32(1)),
+        lambda: m.mla_absorb_query(f32(T * d_in - 1), T, d_in, f32(n_h * d_c * d_in), f32(n_h * d_r * d_in),
+                                   n_h, d_c, d_r, 1e4, i32(T), m.MLA_FP32, f32(T * n_h * d_c),
+                                   f32(T * n_h * d_r), f32(1)),
+        lambda: m.mla_output_proj(f32(T * n_h * d_c), m.MLA_FP32, T, n_h, d_c, d_h, d, m.MLA_PROJ_MERGED,
+                                  f32(d * n_h * d_c - 1), None, f32(T * d)),
+        lambda: m.mla_output_proj(f32(T * n_h * d_c), m.MLA_FP32, T, n_h, d_c, d_h, d, m.MLA_PROJ_TWO_STAGE,
+                                  f32(n_h * d_h * d_c), f32(d * n_h * d_h), f32(T * d - 1)),
+        lambda: m.mla_cache_append(f32(T * d), T, d, f32(d_c * d), f32(d_r * d - 1), d_c, d_r, 1e4,
+                                   i32(T), i32(T), m.MLA_BF16, f32(1), None, f32(1)),
+        lambda: m.mla_cache_write(f32(T * (d_c + d_r)), T, d_c, d_r, 1e4, i32(T - 1), i32(T), m.MLA_BF16,
+                                  f32(1)),
+        lambda: m.mla_fold_query(f32(n_h * d_h * d_in), f32(n_h * d_h * d_c), n_h, d_h, d_c, d_in,
+                                 f32(n_h * d_c * d_in - 1)),
+        lambda: m.mla_fold_output(f32(d * n_h * d_h - 1), f32(n_h * d_h * d_c), n_h, d_h, d_c, d,
+                                  f32(d * n_h * d_c)),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(m.MlaArgumentError):
+            call()
