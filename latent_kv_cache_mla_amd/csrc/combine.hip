@@ -68,7 +68,8 @@ template <> struct Raw8<float> {
   }
 };
 
-// kWR wavefronts per output row (sequence b, row r); a block holds 4 / kWR
+// kWR wavefronts per output row (sequence b, row r); a block of
+// max(4, kWR) wavefronts holds max(4, kWR) / kWR
 // rows. The row's ranges [glo, glo + n) follow from the page prefix sums by
 // the partition arithmetic. Wavefront q takes ranges q, q + kWR, ...: it
 // forms the max m_q and sum s_q of exp(lse_j - m_q) over them and the sum of
@@ -79,7 +80,7 @@ template <> struct Raw8<float> {
 // wavefronts of a row then merge through LDS: M = max m_q,
 // S = sum s_q exp(m_q - M), o = sum_q acc_q exp(m_q - M) / S.
 template <typename PT, int OT, int kWR>  // partial element type, output dtype, waves per row
-__global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ page_start,
+__global__ __launch_bounds__(64 * (kWR > 4 ? kWR : 4)) void combine_kernel(const int32_t* __restrict__ page_start,
                                                       const PT* __restrict__ o_part,
                                                       const float* __restrict__ lse_part,
                                                       const float* __restrict__ l_part,
@@ -87,13 +88,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       float* __restrict__ lse_out,
                                                       int B, int rows, int d_c, int64_t G,
                                                       int skip_whole) {
-  static_assert(kWR == 1 || kWR == 2 || kWR == 4, "waves per row");
-  __shared__ float red[kWR > 1 ? 4 : 1][kWR > 1 ? 64 * 8 : 1];   // per wavefront of the block
-  __shared__ float wms[4][2];                                     // (m_q, s_q) per wavefront
+  static_assert(kWR == 1 || kWR == 2 || kWR == 4 || kWR == 8, "waves per row");
+  constexpr int kWaves = kWR > 4 ? kWR : 4;   // wavefronts per block
+  __shared__ float red[kWR > 1 ? kWaves : 1][kWR > 1 ? 64 * 8 : 1];   // per wavefront of the block
+  __shared__ float wms[kWaves][2];                                     // (m_q, s_q) per wavefront
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int q = wv % kWR;
-  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (4 / kWR) + wv / kWR;
+  const int64_t pair = static_cast<int64_t>(blockIdx.x) * (kWaves / kWR) + wv / kWR;
   if (pair >= static_cast<int64_t>(B) * rows) return;   // uniform per row's wavefronts
   const int64_t b = pair / rows;
   const int r = static_cast<int>(pair % rows);
@@ -258,10 +260,15 @@ void launch_combine_t(const DecodeArgs& a, const PT* op, hipStream_t st) {
   const int64_t per_seq = (a.p->G + B - 1) / B + 1;
   const int64_t resident = static_cast<int64_t>(kNumCUs) * 28;
   int wr = 1;
-  if (per_seq > 16 && pairs * 4 <= resident) wr = 4;
+  if (per_seq > 32 && pairs * 8 <= resident) wr = 8;
+  else if (per_seq > 16 && pairs * 4 <= resident) wr = 4;
   else if (per_seq > 8 && pairs * 2 <= resident) wr = 2;
   const dim3 block(256), grid(static_cast<unsigned>((pairs * wr + 3) / 4));
-  if (wr == 4)
+  if (wr == 8)   // one row per block of eight wavefronts
+    hipLaunchKernelGGL((combine_kernel<PT, OT, 8>), dim3(static_cast<unsigned>(pairs)), dim3(512), 0, st,
+                       a.page_start, op, a.lse_part, a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c,
+                       a.p->G, a.skip_whole ? 1 : 0);
+  else if (wr == 4)
     hipLaunchKernelGGL((combine_kernel<PT, OT, 4>), grid, block, 0, st, a.page_start, op, a.lse_part,
                        a.l_part, a.o_latent, a.lse_out, B, rows, a.d->d_c, a.p->G,
                        a.skip_whole ? 1 : 0);

@@ -67,11 +67,12 @@ def test_full_size_configs(name):
     _check(inp, o, lse, f"{name}-full")
 
 
-@pytest.mark.parametrize("parts", [1, 2, 7, 20, 0])
+@pytest.mark.parametrize("parts", [1, 2, 7, 20, 0, 100])
 def test_split_count_invariance(parts):
     """Results do not depend on the number of page ranges. With 2 sequences of
     24 pages: 1, 2 and 7 ranges merge with one wavefront per row, 20 with two
-    (more than 8 ranges per sequence) and the automatic 48 with four."""
+    (more than 8 ranges per sequence), the automatic 48 with four and 100
+    (more ranges than pages: some are empty) with eight."""
     cfg = wl.scaled(C["c2"], batch=2, seq_len=1500)
     H.say(f"case split-invariance parts={parts}")
     inp = wl.make_decode_inputs(cfg, q_mult=27.7)
