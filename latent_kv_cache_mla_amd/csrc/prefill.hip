@@ -348,13 +348,36 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
                             krb, dr > 0 ? dr : 8, kv + static_cast<int64_t>(nh) * dh, 2 * nh * dh,
                             cu_seqlens, scale, ob, static_cast<int64_t>(nh) * dh, lse, stream);
   if (s != MLA_OK) return s;
-  // 6. out = W^O [o_1 ; ... ; o_{n_h}], with K split into up to four parts
-  // when that fills the last round of 256 workgroups better (320 tiles of
-  // 256 x 256 at 4096 tokens and d 5120 are 1.25 rounds; four splits make five
-  // full ones). The fp32 partial tiles go to the q32 region, which nothing
-  // reads once the attention has run.
+  // 6. out = W^O [o_1 ; ... ; o_{n_h}]. 320 tiles of 256 x 256 at 4096 tokens
+  // and d 5120 are 1.25 rounds of the chip's 256 workgroups; splitting K
+  // fills the last round. The fp32 partial tiles go to the q32 region, which
+  // nothing reads once the attention has run.
   const int KO = nh * dh;
   const int64_t tiles = static_cast<int64_t>((T32 + 255) / 256) * ((D + 255) / 256);
+  // Whole rounds of unsplit tiles first, then the remaining columns with K
+  // split so that they fill one more round: the same matrix work as
+  // splitting every tile, but partial tiles (written, then summed) only for
+  // the remainder (at 4096 tokens and d 5120: 256 tiles over 4096 columns,
+  // then 64 tiles of the last 1024 columns in four splits).
+  {
+    const int tm = (T32 + 255) / 256, tn = (D + 255) / 256;
+    if (tiles > 256 && tiles % 256 != 0 && 256 % tm == 0) {
+      const int n1t = static_cast<int>(tiles / 256) * (256 / tm);   // column tiles left unsplit
+      const int64_t tiles2 = static_cast<int64_t>(tm) * (tn - n1t);
+      const int s2 = tiles2 > 0 ? static_cast<int>(256 / tiles2 < 4 ? 256 / tiles2 : 4) : 0;
+      const int N1 = n1t * 256, N2 = D - N1;
+      if (n1t < tn && s2 >= 2 && N1 % 8 == 0) {
+        const int kps = gemm_bf16_k_per_split(KO, s2);
+        const int gz = (KO + kps - 1) / kps;
+        const size_t need = sizeof(float) * static_cast<size_t>(gz) * static_cast<size_t>(T) * N2;
+        if (kps >= 1024 && need <= L.qb - L.q32) {
+          const uint16_t* wo2 = static_cast<const uint16_t*>(w->W_O) + static_cast<int64_t>(N1) * KO;
+          if ((s = gemm(T32, N1, KO, ob, KO, w->W_O, KO, out, D, 0)) != MLA_OK) return s;
+          return gemm(T32, N2, KO, ob, KO, wo2, KO, out + N1, D, 0, s2, q32);
+        }
+      }
+    }
+  }
   int so = 1;
   double best = static_cast<double>((tiles + 255) / 256);
   for (int sp = 2; sp <= 4; ++sp) {
