@@ -268,3 +268,65 @@ def test_cache_append_at_deepseek_widths():
     ec, ek = _rel(g[slots, :dc], c), _rel(g[slots, dc:], kR)
     H.say(f"  c rel {ec:.2e}, k^R rel {ek:.2e}")
     assert ec < 1e-5 and ek < 1e-5
+
+
+@pytest.mark.parametrize("T,nh,dc,d,o_dtype,offset", [
+    (5, 3, 20, 130, "fp32", 0),    # K = 60: a partial last 32-k stage; 130 outputs: a ragged tile
+    (33, 2, 44, 260, "bf16", 0),   # 33 rows: two row blocks, the second of one row; bf16 rows, 4 at a time
+    (7, 3, 20, 128, "bf16", 2),    # activation rows 4-byte aligned only: bf16 loaded element by element
+    (5, 6, 134, 130, "fp32", 0),   # K = 804 in 7 splits, the last ending 4 k into a stage; split sums element-wise
+    (5, 6, 134, 256, "bf16", 0),   # the same with split sums 4 outputs per thread
+    (4, 2, 21, 64, "fp32", 0),     # K = 42, not a multiple of 4: the vector-ALU GEMM
+    (257, 1, 64, 64, "fp32", 0),   # more than 256 rows: the vector-ALU GEMM
+])
+def test_output_projection_edge_shapes(T, nh, dc, d, o_dtype, offset):
+    """The merged output projection on shapes at the edges of the skinny
+    matrix-core GEMM's fast paths (partial stages, ragged row and output
+    tiles, unaligned bf16 activations) and of its fallback, against the oracle.
+    bf16 activations are compared with the oracle on the same rounded values."""
+    m = H.lib()
+    H.say(f"case output_proj edges T={T} n_h={nh} d_c={dc} d={d} {o_dtype} offset={offset}")
+    rng = np.random.default_rng(40 + T + dc)
+    o = (rng.standard_normal((T, nh, dc)) * 0.05).astype(np.float32)
+    W = (rng.standard_normal((d, nh * dc)) * 0.02).astype(np.float32)
+    if o_dtype == "bf16":
+        o = wl.bf16_round(o)
+        flat = torch.zeros(T * nh * dc + offset, dtype=torch.bfloat16, device="cuda")
+        flat[offset:] = torch.from_numpy(o.reshape(-1)).to(torch.bfloat16).cuda()
+        og = flat[offset:]
+    else:
+        og = _t(o)
+    ref = oracle.output_projection_merged(o.astype(np.float64), W)
+    out = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    wp = torch.empty(max(m.mla_output_proj_workspace_size(T, nh, dc, 0, d, 0), 256), dtype=torch.uint8,
+                     device="cuda")
+    m.mla_output_proj(og, m.DTYPE_CODES[o_dtype], T, nh, dc, 0, d, 0, _t(W), None, out, wp)
+    torch.cuda.synchronize()
+    e = _rel(out.cpu().numpy(), ref)
+    H.say(f"  rel {e:.2e}")
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert e < 1e-5
+
+
+@pytest.mark.parametrize("T,nh,dc,dr,din", [(3, 2, 64, 16, 100), (40, 4, 128, 32, 260)])
+def test_absorb_query_edge_shapes(T, nh, dc, dr, din):
+    """The absorbed query as one GEMM over W_qabs and W_QR (the second matrix's
+    columns start at n_h d_c, a multiple of 128) with a K that ends inside a
+    32-k stage and row counts that are not multiples of 32."""
+    m = H.lib()
+    H.say(f"case absorb_query edges T={T} n_h={nh} d_c={dc} d_R={dr} d_in={din}")
+    rng = np.random.default_rng(50 + T)
+    W_qabs = (rng.standard_normal((nh, dc, din)) * 0.05).astype(np.float32)
+    W_QR = (rng.standard_normal((nh * dr, din)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((T, din)).astype(np.float32)
+    pos = rng.integers(0, 32768, T).astype(np.int32)
+    qa = torch.empty((T, nh, dc), dtype=torch.float32, device="cuda")
+    qr = torch.empty((T, nh, dr), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mla_absorb_query_workspace_size(T, din, nh, dc, dr), dtype=torch.uint8, device="cuda")
+    m.mla_absorb_query(_t(x), T, din, _t(W_qabs), _t(W_QR), nh, dc, dr, 10000.0,
+                       torch.from_numpy(pos).cuda(), m.MLA_FP32, qa, qr, ws)
+    torch.cuda.synchronize()
+    ra, rr = oracle.absorb_query(W_qabs, W_QR, x, pos, 10000.0)
+    ea, er = _rel(qa.cpu().numpy(), ra), _rel(qr.cpu().numpy(), rr)
+    H.say(f"  q_abs rel {ea:.2e}, q_rope rel {er:.2e}")
+    assert ea < 1e-5 and er < 1e-5
