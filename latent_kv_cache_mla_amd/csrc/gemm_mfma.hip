@@ -149,15 +149,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
 // Workgroup = 4 wavefronts in 2 x 2, each 128 x 128 as 4 x 4
 // v_mfma_f32_32x32x16_bf16 tiles (its 256 accumulation registers): every
 // 16-byte fragment read from LDS feeds four MFMAs, against two in the 128 x 128
-// tile. K advances 32 at a time through a ring of four 32 KB LDS stages
-// (A 256 x 32 and B 256 x 32 bf16) filled straight from memory with
-// global_load_lds_dwordx4 (no register round trip), three stages ahead, so
-// that about three stages of matrix work cover the memory latency. A stage
+// tile. K advances 32 at a time through a ring of five 32 KB LDS stages (the
+// whole LDS; A 256 x 32 and B 256 x 32 bf16) filled straight from memory with
+// global_load_lds_dwordx4 (no register round trip), four stages ahead; each
+// stage's fragments are read during the previous stage's MFMAs, so about
+// three stages of matrix work cover the memory latency and one the LDS
+// latency. A stage
 // row is 64 bytes; 16-byte unit u of row r sits at position u ^ ((r >> 2) & 3),
 // which puts the fragment reads of 16 consecutive rows in distinct bank
 // groups. Rows past M or N are read from row M - 1 or N - 1 and their outputs
 // are not stored; the k range of a split must be a multiple of 32.
-constexpr int kLM = 256, kLN = 256, kLK = 32, kLS = 4;
+constexpr int kLM = 256, kLN = 256, kLK = 32, kLS = 5;
 #ifndef MLA_GEMM_BIG_MIN_TILES
 #define MLA_GEMM_BIG_MIN_TILES 240   // smallest grid (tiles x splits) the large tile takes
 #endif
@@ -257,31 +259,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int pre = nst < kLS - 1 ? nst : kLS - 1;
-  for (int st = 0; st < pre; ++st) issue(st);
-  for (int st = 0; st < nst; ++st) {
-    // stage st has landed when at most the copies of the stages issued after
-    // it (up to two) are still in flight
-    const int later = min(nst - 1 - st, kLS - 2);
-    if (later >= 2) GEMM_WAIT_VM(2 * kLCopies);
-    else if (later == 1) GEMM_WAIT_VM(kLCopies);
-    else GEMM_WAIT_VM(0);
-    // every wavefront's copies of stage st are visible, and every wavefront
-    // is done with stage st - 1, whose buffer the next copy refills
-    __syncthreads();
-    // the copies of stage st + 3 go out one per four MFMAs below: issued all
-    // at once they would stall the wavefront on the memory queue
-    const bool cp = st + kLS - 1 < nst;
-    const uint8_t* csrc = mat + 2LL * (kb + kLK * (st + kLS - 1));
-    asm volatile("" : "+s"(csrc));
-    const uint32_t cdst = lds0 + ((st + kLS - 1) % kLS) * kLStage + dst0;
+  // Software pipeline over a five-slot ring: the 16 fragments of stage st + 1
+  // are read from LDS while the 32 MFMAs of stage st run (two fragment sets,
+  // alternating at compile time through pairs of steps), so the LDS latency
+  // is hidden behind matrix work. The copies of stage st + 4 go out during
+  // step st's MFMAs into the slot of stage st - 1, whose fragments every
+  // wavefront read during step st - 2, before the barrier of step st - 1.
+  // At the top of step st, stage st + 1 must have landed (issued three steps
+  // earlier): the copies of stages st + 2 and st + 3 may still be in flight.
+  typedef bf16x8_t Frags[2][4];
+  auto read_frags = [&](int st, Frags& a, Frags& b) {
     const uint32_t sb = lds0 + (st % kLS) * kLStage;
     const uint32_t sa = sb + wm * 128 * 64, sbb = sb + kLM * kLK * 2 + wn * 128 * 64;
-    // all 16 fragments of the stage are read before its first MFMA (the
-    // scheduling barrier keeps the compiler from trading them for registers
-    // by reloading one fragment per group of MFMAs, which would expose the LDS
-    // latency four times per k step)
-    bf16x8_t a[2][4], b[2][4];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -289,7 +278,25 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
         a[kk][i] = frag(sa + i * 32 * 64 + (kk ? fb : fa));
         b[kk][i] = frag(sbb + i * 32 * 64 + (kk ? fb : fa));
       }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_for = [&](int st) {   // stage st has landed; later issued stages may be in flight
+    const int later = min(nst - 1 - st, kLS - 3);
+    if (later >= 2) GEMM_WAIT_VM(2 * kLCopies);
+    else if (later == 1) GEMM_WAIT_VM(kLCopies);
+    else GEMM_WAIT_VM(0);
+  };
+  auto step = [&](int st, Frags& a, Frags& b, Frags& na, Frags& nb) {
+    if (st + 1 < nst) {
+      wait_for(st + 1);
+      __syncthreads();
+      read_frags(st + 1, na, nb);
+    }
+    // (the copies of stage st + 4 go out one per four MFMAs: issued all at
+    // once they would stall the wavefront on the memory queue)
+    const bool cp = st + kLS - 1 < nst;
+    const uint8_t* csrc = mat + 2LL * (kb + kLK * (st + kLS - 1));
+    asm volatile("" : "+s"(csrc));
+    const uint32_t cdst = lds0 + ((st + kLS - 1) % kLS) * kLStage + dst0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -298,9 +305,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
         if (cp) dma16(csrc, voff[4 * kk + i], cdst + 1024 * (4 * kk + i));
-        __builtin_amdgcn_sched_barrier(0);
       }
+  };
+  const int pre = nst < kLS - 1 ? nst : kLS - 1;
+  for (int st = 0; st < pre; ++st) issue(st);
+  Frags a0, b0, a1, b1;
+  if (nst > 0) {
+    // stage 0 has landed when at most the copies of stages 1 .. 3 are in flight
+    const int later = min(nst - 1, kLS - 2);
+    if (later >= 3) GEMM_WAIT_VM(3 * kLCopies);
+    else if (later == 2) GEMM_WAIT_VM(2 * kLCopies);
+    else if (later == 1) GEMM_WAIT_VM(kLCopies);
+    else GEMM_WAIT_VM(0);
+    __syncthreads();
+    read_frags(0, a0, b0);
   }
+  // (pairs of steps with no test between them, then the odd last step: a
+  // test inside the pair made the compiler copy the accumulators between
+  // register files every pair)
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    step(st, a0, b0, a1, b1);
+    step(st + 1, a1, b1, a0, b0);
+  }
+  if (st < nst) step(st, a0, b0, a1, b1);
 
   // acc[i][j] register r holds C[m][n] with m = 8 (r / 4) + 4 half + r % 4 and
   // n = l32 within the 32 x 32 tile (i, j) of the wavefront's 128 x 128 block
