@@ -13,8 +13,8 @@
 //
 // Workgroup = (query tile of 128 positions, head, sequence); 4 wavefronts of
 // 32 query rows. Keys and values stream through a double-buffered LDS tile of
-// 32 positions, shared by the four wavefronts; the next tile's global loads
-// are in flight while the current one is multiplied.
+// 32 positions, shared by the four wavefronts, copied straight from global
+// memory (global_load_lds_dwordx4) one tile ahead of the one multiplied.
 //   * scores S^T [32 keys x 32 queries] = K Q^T with v_mfma_f32_32x32x16_bf16,
 //     keys as the M dimension: A = key rows from LDS, B = the wavefront's
 //     queries, held in registers for the whole pass. Each lane then holds 16
@@ -26,9 +26,8 @@
 //   * O^T [d_v x 32 queries] += V^T P^T: P^T straight from the score
 //     registers (bf16), V^T read from the row-major value tile with the LDS
 //     transpose load in the key order that matches the score registers.
-// LDS rows are padded (keys: 16 bytes, values: 64 bytes) so that the 16-byte
-// key-fragment reads and the transposed value reads are free of bank
-// conflicts.
+// The LDS layout of a tile (TileRegion below) keeps the 16-byte key-fragment
+// reads and the transposed value reads free of bank conflicts.
 #include <algorithm>
 
 #include "internal.h"
@@ -188,8 +187,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillAttnArgs a)
   __syncthreads();
   // tiles from n_vis on start after the wavefront's last query: fully
   // masked, the wavefront only takes part in their copies and barriers (two
-  // loops rather than a test in one, so that O stays in the same registers)
-  const int n_vis = min(n_kt, w_last / kKT + 1);
+  // loops rather than a test in one, so that O stays in the same registers);
+  // a wavefront whose rows all lie past the sequence end computes none
+  const int n_vis = q0 + 32 * w >= S ? 0 : min(n_kt, w_last / kKT + 1);
   int kt = 0;
   for (; kt < n_vis; ++kt) {
     const int buf = kt & 1;
