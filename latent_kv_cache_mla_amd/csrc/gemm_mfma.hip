@@ -14,8 +14,11 @@
 // 2 x 2 v_mfma_f32_32x32x16_bf16 tiles. K advances 64 at a time through a
 // double-buffered LDS tile whose rows are padded to 144 bytes: the 16-byte
 // fragment reads of 8 or 16 consecutive rows then fall in distinct bank
-// groups. The next K step's global loads are in flight during the current
-// step's MFMAs. Rows past M or N and K steps past the end load zeros.
+// groups. Global loads go through three register sets: a K step's loads
+// are issued three steps before its chunks are stored to LDS, so two steps of
+// matrix work besides the current one cover their latency. Rows past M or N
+// read the last row (their outputs are not stored), and A chunks past the end
+// of a split's k range are zeroed in LDS.
 // Split-K (for skinny M, where the output tiles alone do not fill the chip)
 // writes fp32 partial tiles that a second kernel sums in split order.
 #include <type_traits>
@@ -28,6 +31,45 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+
+// Epilogue stores of the large tile. Its MFMAs take the B fragment as their
+// first operand, so accumulator tile (i, j) holds C^T: register 4 q + e of
+// lane (half, l32) is C[l32][8 q + 4 half + e] of the 32 x 32 tile, and each
+// lane stores runs of four consecutive outputs of one row with one 16-byte
+// (fp32) or 8-byte (bf16) store (measured on the prefill projections: 0.242
+// -> 0.230 ms at 4096 x 16384 x 1536 with a bf16 output, 0.122 -> 0.113 ms at
+// 4096 x 8192 x 1536 with an fp32 one; on the 128 x 128 tile the same stores
+// were 4% slower than one output per store). wide_ok: the row stride is a
+// multiple of 4 and the base is aligned for those stores; otherwise, and in
+// tiles at the edge of C, the four outputs go one by one, each within bounds.
+__device__ __forceinline__ void put4(float* q, f32x4v_t v) { *reinterpret_cast<f32x4v_t*>(q) = v; }
+__device__ __forceinline__ void put4(uint16_t* q, f32x4v_t v) {
+  u32x2v_t u;
+  u[0] = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+  u[1] = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<u32x2v_t*>(q) = u;
+}
+__device__ __forceinline__ void put1(float* q, float v) { *q = v; }
+__device__ __forceinline__ void put1(uint16_t* q, float v) { *q = f32_to_bf16(v); }
+template <class T>
+__device__ __forceinline__ bool wide_ok(const T* base, int64_t ld) {
+  return (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(base) & (4 * sizeof(T) - 1)) == 0;
+}
+// four outputs v of row m, columns n .. n + 3
+template <class T>
+__device__ __forceinline__ void store_run(T* base, int64_t ld, int64_t m, int64_t n, f32x4v_t v,
+                                          bool fast, int64_t M, int64_t N) {
+  if (fast) {
+    put4(base + m * ld + n, v);
+  } else if (m < M) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) put1(base + m * ld + n + e, v[e]);
+  }
+}
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kPitch = kBK + 8;   // elements per LDS row (144 bytes)
@@ -48,9 +90,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
   // row c / 8 = tid / 8 + 32 j, elements 8 (tid % 8) .. + 7. The row
   // pointers are formed once; rows past M or N read the last row (their
   // outputs are not stored). Every stage runs the same loads: a chunk at or
-  // past K reads the row's last chunk instead (finite values), and A chunks
-  // at or past the split's end are zeroed when the stage is stored to LDS,
-  // which zeroes their products.
+  // past the split's end reads the split's last chunk of the row instead
+  // (finite values, already cached), and A chunks at or past the split's end
+  // are zeroed when the stage is stored to LDS, which zeroes their products.
   const int r8 = tid >> 3, kc = (tid & 7) * 8;
   const uint16_t* pa[4];
   const uint16_t* pb[4];
@@ -59,25 +101,31 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
     pa[j] = g.A + min(m0 + r8 + 32 * j, static_cast<int64_t>(g.M) - 1) * g.lda + kc;
     pb[j] = g.B + min(n0 + r8 + 32 * j, static_cast<int64_t>(g.N) - 1) * g.ldb + kc;
   }
-  const int klim = g.K - 8 - kc;   // the last chunk start of a row, minus kc
+  const int klim = ke - 8 - kc;   // the split's last chunk start in a row, minus kc
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  u32x4_t ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // kPF register sets of staged chunks: the loads of step s + kPF are issued
+  // at the start of step s, so a load has kPF - 1 whole steps of matrix work
+  // and the step it is issued in to arrive before its chunks go to LDS.
+  constexpr int kPF = 3;
+  u32x4_t ra[kPF][4], rb[kPF][4];
+  auto gload = [&](auto SET, int k0) {
+    constexpr int st = decltype(SET)::value;
     const int kk = min(k0, klim);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ra[j] = *reinterpret_cast<const u32x4_t*>(pa[j] + kk);
-      rb[j] = *reinterpret_cast<const u32x4_t*>(pb[j] + kk);
+      ra[st][j] = *reinterpret_cast<const u32x4_t*>(pa[j] + kk);
+      rb[st][j] = *reinterpret_cast<const u32x4_t*>(pb[j] + kk);
     }
   };
-  auto swrite = [&](int buf, int k0) {
+  auto swrite = [&](auto SET, int buf, int k0) {
+    constexpr int st = decltype(SET)::value;
     // 0 for A chunks at or past the split's end (the first test is uniform)
     const uint32_t keep = k0 + kBK > ke && k0 + kc >= ke ? 0u : ~0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = r8 + 32 * j;
-      *reinterpret_cast<u32x4_t*>(&As[buf][row * kPitch + kc]) = ra[j] & keep;
-      *reinterpret_cast<u32x4_t*>(&Bs[buf][row * kPitch + kc]) = rb[j];
+      *reinterpret_cast<u32x4_t*>(&As[buf][row * kPitch + kc]) = ra[st][j] & keep;
+      *reinterpret_cast<u32x4_t*>(&Bs[buf][row * kPitch + kc]) = rb[st][j];
     }
   };
 
@@ -87,15 +135,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  if (kb < ke) {
-    gload(kb);
-    swrite(0, kb);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = kb; k0 < ke; k0 += kBK) {
-    const bool more = k0 + kBK < ke;
-    if (more) gload(k0 + kBK);
+  auto mfmas = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int col = kk * 16 + half * 8;
@@ -111,10 +151,35 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(MfmaGemmArgs g, int k
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) swrite(buf ^ 1, k0 + kBK);
+  };
+  typedef std::integral_constant<int, 0> S0;
+  typedef std::integral_constant<int, 1> S1;
+  typedef std::integral_constant<int, 2> S2;
+  static_assert(kPF == 3, "the step sequence below names three sets");
+  // step s: its chunks are in LDS buffer s % 2 and came from set s % kPF,
+  // which is free again; the next step's chunks wait in set (s + 1) % kPF.
+  auto step = [&](auto SET, int s) {
+    constexpr int st = decltype(SET)::value;
+    const int k0 = kb + s * kBK;
+    gload(SET, k0 + kPF * kBK);
+    mfmas(s & 1);
+    swrite(std::integral_constant<int, (st + 1) % kPF>{}, (s + 1) & 1, k0 + kBK);
     __syncthreads();
-    buf ^= 1;
+  };
+  const int n = kb < ke ? (ke - kb + kBK - 1) / kBK : 0;   // K steps of this split
+  gload(S0{}, kb);
+  gload(S1{}, kb + kBK);
+  gload(S2{}, kb + 2 * kBK);
+  swrite(S0{}, 0, kb);
+  __syncthreads();
+  int s = 0;
+  for (; s + kPF <= n; s += kPF) {
+    step(S0{}, s);
+    step(S1{}, s + 1);
+    step(S2{}, s + 2);
   }
+  if (s < n) step(S0{}, s);
+  if (s + 1 < n) step(S1{}, s + 1);
 
   // acc[i][j] register r holds C[m][n] with m = 8 (r / 4) + 4 half + r % 4 and
   // n = l32 within the 32 x 32 tile (i, j). One pass per output form; the
@@ -303,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], b[kk][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[kk][j], a[kk][i], acc[i][j], 0, 0, 0);
         if (cp) dma16(csrc, voff[4 * kk + i], cdst + 1024 * (4 * kk + i));
       }
   };
@@ -330,37 +395,38 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
   }
   if (st < nst) step(st, a0, b0, a1, b1);
 
-  // acc[i][j] register r holds C[m][n] with m = 8 (r / 4) + 4 half + r % 4 and
-  // n = l32 within the 32 x 32 tile (i, j) of the wavefront's 128 x 128 block
-  const int64_t mw = m0 + wm * 128 + 4 * half, nw = n0 + wn * 128 + l32;
-  // one pass per output form, the bounds tests only on edge tiles
-  auto store_all = [&](auto put) {
-    const bool edge = m0 + kLM > g.M || n0 + kLN > g.N;
+  // acc[i][j] holds C^T of the 32 x 32 tile (i, j) of the wavefront's
+  // 128 x 128 block (see store_run); one pass per output form, the bounds
+  // tests only on edge tiles
+  const bool edge = m0 + kLM > g.M || n0 + kLN > g.N;
+  const int64_t mw = m0 + wm * 128 + l32, nw = n0 + wn * 128 + 4 * half;
+  auto store_all = [&](auto* base, int64_t ld) {
+    const bool fast = !edge && wide_ok(base, ld);
     static_for4([&](auto I) {
       static_for4([&](auto J) {
         constexpr int i = decltype(I)::value, j = decltype(J)::value;
-        const int64_t n = nw + j * 32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = mw + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (!edge || (m < g.M && n < g.N)) put(m, n, acc[i][j][r]);
-        }
-        // one tile's stores at a time (the addresses of all 256 would not
+        // (the empty asm keeps each tile's reads of the accumulation
+        // registers next to its stores: hoisted ahead of the three output
+        // forms, they would need more vector registers than there are)
+        asm volatile("" : "+a"(acc[i][j]));
+        static_for4([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          store_run(base, ld, mw + i * 32, nw + j * 32 + 8 * q,
+                    __builtin_shufflevector(acc[i][j], acc[i][j], 4 * q, 4 * q + 1, 4 * q + 2, 4 * q + 3),
+                    fast, g.M, g.N);
+        });
+        // one tile's stores at a time (the addresses of all 64 would not
         // fit the registers)
         __builtin_amdgcn_sched_barrier(0);
       });
     });
   };
-  if (g.splits > 1) {
-    float* part = g.partial + static_cast<int64_t>(kz) * g.M * g.N;
-    store_all([&](int64_t m, int64_t n, float v) { part[m * g.N + n] = v; });
-  } else if (g.c_bf16) {
-    uint16_t* c = static_cast<uint16_t*>(g.C);
-    store_all([&](int64_t m, int64_t n, float v) { c[m * g.ldc + n] = f32_to_bf16(v); });
-  } else {
-    float* c = static_cast<float*>(g.C);
-    store_all([&](int64_t m, int64_t n, float v) { c[m * g.ldc + n] = v; });
-  }
+  if (g.splits > 1)
+    store_all(g.partial + static_cast<int64_t>(kz) * g.M * g.N, static_cast<int64_t>(g.N));
+  else if (g.c_bf16)
+    store_all(static_cast<uint16_t*>(g.C), g.ldc);
+  else
+    store_all(static_cast<float*>(g.C), g.ldc);
 }
 
 // C = sum over the splits of the fp32 partial tiles, in split order.
