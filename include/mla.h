@@ -140,9 +140,11 @@ mla_status mla_decode(const mla_decode_desc* d, const void* q_abs, const void* q
                       void* o_latent, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* The two halves of mla_decode, for callers that merge partials themselves
- * (for example after gathering them from several devices that each hold a
- * token range of the same sequences).
+/* The two halves of mla_decode as separate calls, for callers that want the
+ * split-KV kernel and the merge as two launches (to time them apart, or to run
+ * other work on the stream between them). The partials stay in the
+ * workspace in a layout private to the library, so only mla_decode_combine
+ * can merge them, and only for the same desc, seq_lens and workspace.
  *
  * mla_decode_partial: the plan (unless plan_ready) and the split-KV kernel
  * only. It leaves, in the workspace, the partial output and log-sum-exp of
@@ -181,9 +183,12 @@ mla_status mla_decode_noalloc(const mla_decode_desc* d, const void* q_abs, const
 size_t mla_decode_noalloc_max_workspace(void);
 
 /* Debug check of device contents (synchronises `stream`, copies to host):
- * every page id a sequence uses is in [0, n_pages), and every length is in
- * [0, 64 * max_blocks_per_seq]. Returns MLA_ERR_BAD_CONTENTS on the first
- * violation, with its position in mla_last_error(). */
+ * every page id a sequence uses is in [0, n_pages), every length is in
+ * [0, 64 * max_blocks_per_seq], and every non-empty sequence holds at least
+ * q_len tokens (its own queries are cached before attention; mla_decode still
+ * gives a query at a negative position o = 0 and lse = -inf). Returns
+ * MLA_ERR_BAD_CONTENTS on the first violation, with its position in
+ * mla_last_error(). */
 mla_status mla_decode_validate(const mla_decode_desc* d, const int32_t* seq_lens,
                                const int32_t* block_table, int64_t n_pages, void* stream);
 

@@ -309,6 +309,11 @@ mla_status mla_decode_validate(const mla_decode_desc* d, const int32_t* seq_lens
     if (S < 0 || static_cast<int64_t>(S) > static_cast<int64_t>(kPage) * d->max_blocks_per_seq)
       return fail(MLA_ERR_BAD_CONTENTS, "seq_lens[%d] = %d outside [0, %d]", b, S,
                   kPage * d->max_blocks_per_seq);
+    // a non-empty sequence holds its own query tokens (they are appended to
+    // the cache before attention), so it is at least q_len long
+    if (S > 0 && S < d->q_len)
+      return fail(MLA_ERR_BAD_CONTENTS, "seq_lens[%d] = %d is shorter than q_len = %d", b, S,
+                  d->q_len);
     for (int64_t k = 0; k < pages_of(S); ++k) {
       const int32_t pg = bt[static_cast<size_t>(b) * d->max_blocks_per_seq + k];
       if (pg < 0 || pg >= n_pages)

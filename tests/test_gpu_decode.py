@@ -216,6 +216,18 @@ def test_validate_catches_bad_contents():
     long = torch.tensor([130, 64 * dev["max_blocks"] + 1], dtype=torch.int32, device="cuda")
     with pytest.raises(m.MlaError):
         m.mla_decode_validate(desc, long, dev["block_table"], dev["n_pages"])
+    # with two query tokens a non-empty sequence needs at least two cached
+    # tokens; an empty one is still accepted
+    desc2 = m.decode_desc(cfg.batch, 2, cfg.n_heads, cfg.d_c, cfg.d_rope, dev["max_blocks"])
+    m.mla_decode_validate(desc2, dev["seq_lens"], dev["block_table"], dev["n_pages"])
+    for lens, ok in (([0, 2], True), ([1, 130], False)):
+        t = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        if ok:
+            m.mla_decode_validate(desc2, t, dev["block_table"], dev["n_pages"])
+        else:
+            with pytest.raises(m.MlaError) as e:
+                m.mla_decode_validate(desc2, t, dev["block_table"], dev["n_pages"])
+            assert e.value.status == m.MLA_ERR_BAD_CONTENTS
 
 
 def test_batch_above_the_in_kernel_prefix_limit():
