@@ -32,10 +32,28 @@ Modules:
   formats    — bf16 and fp8 e4m3 decoding/encoding from their definitions.
   closed_forms — per-token cache sizes and operation counts.
 
-Parity unpinned: no page prints a numerical attention output, seed or RNG
-stream; agreement with the pages' own numbers is pinned only through their
-identities and closed forms. The RoPE pair layout and rotation direction are
-a free choice (any fixed choice preserves the relative-position property).
+Pins (tests/test_oracle_pins.py, tests/test_oracle_mutations.py). No page
+prints a numerical attention output, seed or RNG stream, so the functions are
+pinned to what the pages and the mathematics fix rather than to printed
+outputs:
+  * mla_unabsorbed (O1): its scores against a pure-Python brute force at the
+    DeepSeek head widths, with the score scale pinned to the pages'
+    denominator sqrt(d_h + d_R);
+  * mla_absorbed (O2), and through it fold_query, fold_output, cache_append,
+    absorb_query, latent_attention and output_projection_merged: O2 equals O1
+    to 1e-10 on the tiny config and on random shapes (the associativity the
+    pages box), so a dropped term or a wrong index in any of them fails;
+  * latent_attention (O3): brute force on tiny inputs, single-token, zero
+    query, planted spike, empty sequence and causal-pair special cases;
+  * output_projection_two_stage: equals the merged form (the same
+    reassociation); expanded_attention: equals O1 at every position and a
+    written-out three-position case;
+  * softmax against scipy; rope against complex rotation, the identity at
+    position 0, norm preservation and the relative-position property (the
+    pair layout and rotation direction are a free choice that these fix up
+    to that choice);
+  * formats against torch on all 256 e4m3 codes and on bf16; closed_forms
+    against the sizes and ratios the pages print (tests/golden/).
 """
 from .reference import (  # noqa: F401
     rope, softmax, score_scale, expanded_attention, mla_unabsorbed, mla_absorbed, latent_attention,
