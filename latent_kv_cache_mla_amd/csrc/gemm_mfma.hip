@@ -421,8 +421,37 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(MfmaGemmArgs g, i
       });
     });
   };
+  // the same stores with the run's two pairs rotated first (a run of four
+  // outputs starts at a multiple of 4, so it holds whole pairs of one block)
+  auto store_all_rope = [&](uint16_t* base, int64_t ld) {
+    const bool fast = !edge && wide_ok(base, ld);
+    const int dr = g.rope_dr;
+    static_for4([&](auto I) {
+      static_for4([&](auto J) {
+        constexpr int i = decltype(I)::value, j = decltype(J)::value;
+        asm volatile("" : "+a"(acc[i][j]));
+        const int64_t m = mw + i * 32;
+        const float* cs = g.rope_cs + min(m, static_cast<int64_t>(g.M) - 1) * dr;
+        static_for4([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int64_t n = nw + j * 32 + 8 * q;
+          f32x4v_t v = __builtin_shufflevector(acc[i][j], acc[i][j], 4 * q, 4 * q + 1, 4 * q + 2, 4 * q + 3);
+          const f32x4v_t t = *reinterpret_cast<const f32x4v_t*>(cs + n % dr);
+          const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+          v[0] = a0 * t[0] - b0 * t[1];
+          v[1] = a0 * t[1] + b0 * t[0];
+          v[2] = a1 * t[2] - b1 * t[3];
+          v[3] = a1 * t[3] + b1 * t[2];
+          store_run(base, ld, m, n, v, fast, g.M, g.N);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  };
   if (g.splits > 1)
     store_all(g.partial + static_cast<int64_t>(kz) * g.M * g.N, static_cast<int64_t>(g.N));
+  else if (g.rope_cs != nullptr)
+    store_all_rope(static_cast<uint16_t*>(g.C), g.ldc);
   else if (g.c_bf16)
     store_all(static_cast<uint16_t*>(g.C), g.ldc);
   else
@@ -500,6 +529,11 @@ mla_status launch_gemm_bf16(const MfmaGemmArgs& g, hipStream_t st) {
   const bool big = g.K % kLK == 0 && big_tiles >= MLA_GEMM_BIG_MIN_TILES && kps >= MLA_GEMM_BIG_MIN_K &&
                    static_cast<int64_t>(g.M) * g.lda * 2 < (1LL << 32) &&
                    static_cast<int64_t>(g.N) * g.ldb * 2 < (1LL << 32);
+  if (g.rope_cs != nullptr &&
+      (!big || gz > 1 || !g.c_bf16 || g.rope_dr < 4 || g.rope_dr % 4 != 0 || g.N % g.rope_dr != 0 ||
+       (reinterpret_cast<uintptr_t>(g.rope_cs) & 15) != 0))
+    return fail(MLA_ERR_UNSUPPORTED, "bf16 GEMM: RoPE in the epilogue needs the large tile, no split, "
+                                     "a bf16 output and whole 4-aligned rope blocks");
   if (big) {
     const int tm = (g.M + kLM - 1) / kLM, tn = (g.N + kLN - 1) / kLN;
     const int tiles = tm * tn * gz;

@@ -114,6 +114,12 @@ struct MfmaGemmArgs {
   void* C; int64_t ldc; int c_bf16;
   int splits;
   float* partial;
+  // RoPE in the epilogue (bf16 output, no split, the 256 x 256 tile only;
+  // launch_gemm_bf16 returns MLA_ERR_UNSUPPORTED otherwise): outputs
+  // (2k, 2k + 1) of every rope_dr-column block of row m are rotated by the
+  // angle whose cosine and sine are rope_cs[m * rope_dr + 2 k] and [.. + 1]
+  const float* rope_cs = nullptr;
+  int rope_dr = 0;
 };
 mla_status launch_gemm_bf16(const MfmaGemmArgs& g, hipStream_t st);
 int gemm_bf16_k_per_split(int K, int splits);

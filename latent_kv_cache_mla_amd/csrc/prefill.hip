@@ -125,6 +125,21 @@ __global__ __launch_bounds__(256) void rope_round8_kernel(float* __restrict__ X,
   }
 }
 
+// cos and sin of every (row, pair) angle, fp64 as in rope_round8_kernel:
+// cs[t * d_r + 2 k] = cos(pos_t theta^(-2k/d_r)), cs[t * d_r + 2 k + 1] = sin(..)
+__global__ __launch_bounds__(256) void rope_table_kernel(const int32_t* __restrict__ positions, int64_t T,
+                                                         int d_r, double theta, float* __restrict__ cs) {
+  const int half_r = d_r / 2;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= T * half_r) return;
+  const int64_t t = e / half_r;
+  const int k = static_cast<int>(e % half_r);
+  float c, sn;
+  rope_cs(positions[t], k, d_r, theta, &c, &sn);
+  cs[t * d_r + 2 * k] = c;
+  cs[t * d_r + 2 * k + 1] = sn;
+}
+
 mla_status launch_rope_round(float* X, int64_t ldx, int width, int r0, int n_rope, int d_r,
                              const int32_t* positions, float theta, uint16_t* Y, int64_t ldy,
                              int write_back, int64_t T, hipStream_t st) {
@@ -336,10 +351,30 @@ mla_status mla_prefill(const mla_prefill_desc* d, const void* h, int64_t T, cons
   if ((s = gemm(T32, QC, din, x, din, w->W_UQR, din, qb, QW, 1)) != MLA_OK) return s;
   if (dr > 0) {
     const uint16_t* wqr = static_cast<const uint16_t*>(w->W_UQR) + static_cast<int64_t>(QC) * din;
-    if ((s = gemm(T32, QR, din, x, din, wqr, din, q32, QR, 0)) != MLA_OK) return s;
-    if ((s = launch_rope_round(q32, QR, QR, 0, nh, dr, positions, d->rope_theta, qb + QC, QW, 0, T,
-                               st)) != MLA_OK)
-      return s;
+    // where the large tile takes it, q^R leaves its GEMM rotated and in bf16
+    // (the angles from a table of T x d_R values in the q32 region); else the
+    // fp32 GEMM and the RoPE pass
+    bool fused = false;
+    if (dr % 4 == 0) {
+      const int64_t n_ang = static_cast<int64_t>(T) * (dr / 2);
+      hipLaunchKernelGGL(rope_table_kernel, dim3(static_cast<unsigned>((n_ang + 255) / 256)), dim3(256), 0, st,
+                         positions, static_cast<int64_t>(T), dr, static_cast<double>(d->rope_theta), q32);
+      if (hipGetLastError() != hipSuccess) return fail(MLA_ERR_HIP, "rope table launch failed");
+      MfmaGemmArgs g{};
+      g.M = T32; g.N = QR; g.K = din; g.A = x; g.lda = din; g.B = wqr; g.ldb = din;
+      g.C = qb + QC; g.ldc = QW; g.c_bf16 = 1; g.splits = 1; g.partial = nullptr;
+      g.rope_cs = q32; g.rope_dr = dr;
+      s = launch_gemm_bf16(g, st);
+      if (s == MLA_OK) fused = true;
+      else if (s != MLA_ERR_UNSUPPORTED) return s;
+      else clear_error();
+    }
+    if (!fused) {
+      if ((s = gemm(T32, QR, din, x, din, wqr, din, q32, QR, 0)) != MLA_OK) return s;
+      if ((s = launch_rope_round(q32, QR, QR, 0, nh, dr, positions, d->rope_theta, qb + QC, QW, 0, T,
+                                 st)) != MLA_OK)
+        return s;
+    }
   }
   // 4. expanded keys and values [k^C ; v] = [W^UK ; W^UV] c
   if ((s = gemm(T32, 2 * nh * dh, dc, cb, dc, w->W_UKV, dc, kv, 2 * nh * dh, 1)) != MLA_OK) return s;
