@@ -31,6 +31,26 @@ def lib():
 from workloads.device import device_inputs, to_dev  # noqa: E402,F401
 
 
+GUARD = 4096          # guard bytes on each side of a guarded buffer
+PATTERN = 0x5A
+
+
+class Guarded:
+    """A device buffer of `shape` and `dtype` between two guard regions; the
+    inside starts as `fill` (a byte)."""
+
+    def __init__(self, shape, dtype, fill=0xFF):
+        esz = torch.empty((), dtype=dtype).element_size()
+        self.n = int(np.prod(shape)) * esz
+        self.big = torch.full((GUARD + self.n + GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
+        self.big[GUARD:GUARD + self.n] = fill
+        self.t = self.big[GUARD:GUARD + self.n].view(dtype).view(shape)
+
+    def guards_intact(self):
+        g = self.big.cpu().numpy()
+        return bool(np.all(g[:GUARD] == PATTERN) and np.all(g[GUARD + self.n:] == PATTERN))
+
+
 def run_decode(inp: wl.DecodeInputs, num_partitions: int = 0, dev=None, poison: bool = True,
                plan_separately: bool = False, with_lse: bool = True, scale: float | None = None,
                flags: int = 0):

@@ -223,3 +223,35 @@ def test_prefill_layer_matches_the_unabsorbed_definition(name):
     lat_err = np.abs(g_lat - ref_lat)
     H.say(f"  [{name}] latent max-abs {float(lat_err.max()):.3e}")
     assert np.all(lat_err <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("name", ["prefill-tiny", "prefill-mid"])
+def test_prefill_writes_only_its_outputs(name):
+    """The layer with its output, latent rows, log-sum-exp and workspace each
+    between guard regions: no guard byte changes, and the results equal those
+    of the plain call bitwise (its kernels use no atomics: every sum has a
+    fixed order)."""
+    m = H.lib()
+    pcfg = P[name]
+    H.say(f"case prefill guards {name} lens={pcfg.seq_lens}")
+    model = wl.make_prefill_model(pcfg)
+    out0, lat0, lse0 = _run_prefill(pcfg, model)
+    lay = wl.prefill_gpu_layout(model)
+    T = pcfg.T
+    d = m.prefill_desc(len(pcfg.seq_lens), max(pcfg.seq_lens), pcfg.d_model, pcfg.n_heads,
+                       pcfg.d_head, pcfg.d_rope, pcfg.d_c, pcfg.d_cq, pcfg.rope_theta)
+    ws = H.Guarded((m.mla_prefill_workspace_size(d, T),), torch.uint8)
+    out = H.Guarded((T, pcfg.d_model), torch.float32)
+    lat = H.Guarded((T, pcfg.d_c + pcfg.d_rope), torch.float32)
+    lse = H.Guarded((pcfg.n_heads, T), torch.float32)
+    w = {k: (None if v is None else bf16_dev(v)) for k, v in lay.items() if k != "h"}
+    m.mla_prefill(d, bf16_dev(lay["h"]), torch.from_numpy(wl.prefill_cu_seqlens(pcfg.seq_lens)).cuda(),
+                  torch.from_numpy(wl.prefill_positions(pcfg.seq_lens)).cuda(), w,
+                  pcfg.softmax_scale, out.t, lat.t, lse.t, ws.t)
+    torch.cuda.synchronize()
+    for buf, nm in ((out, "the output"), (lat, "the latent rows"), (lse, "the log-sum-exp"),
+                    (ws, "the workspace")):
+        assert buf.guards_intact(), f"a store landed outside {nm}"
+    assert np.array_equal(out.t.cpu().numpy().astype(np.float64), out0)
+    assert np.array_equal(lat.t.cpu().numpy().astype(np.float64), lat0)
+    assert np.array_equal(lse.t.cpu().numpy().astype(np.float64), lse0)

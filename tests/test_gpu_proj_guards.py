@@ -16,9 +16,6 @@ from tests import gpu_harness as H
 
 pytestmark = pytest.mark.gpu
 
-GUARD = 4096          # guard bytes on each side of every buffer
-PATTERN = 0x5A
-
 
 def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
@@ -28,20 +25,7 @@ def _rel(g, r):
     return float(np.linalg.norm(np.asarray(g, np.float64) - r) / np.linalg.norm(r))
 
 
-class Guarded:
-    """A device buffer of `shape` and `dtype` between two guard regions; the
-    inside starts as `fill` (a byte)."""
-
-    def __init__(self, shape, dtype, fill=0xFF):
-        esz = torch.empty((), dtype=dtype).element_size()
-        self.n = int(np.prod(shape)) * esz
-        self.big = torch.full((GUARD + self.n + GUARD,), PATTERN, dtype=torch.uint8, device="cuda")
-        self.big[GUARD:GUARD + self.n] = fill
-        self.t = self.big[GUARD:GUARD + self.n].view(dtype).view(shape)
-
-    def guards_intact(self):
-        g = self.big.cpu().numpy()
-        return bool(np.all(g[:GUARD] == PATTERN) and np.all(g[GUARD + self.n:] == PATTERN))
+Guarded = H.Guarded
 
 
 def _workspace(nbytes):
